@@ -1,0 +1,124 @@
+/*
+ * tq.h -- C ABI of the turbo3 / turbo2 KV-cache block codec for AMD MI355X
+ * (gfx950).  Plain C: no C++ types, no exceptions and no torch types cross
+ * this boundary.
+ *
+ * The method is the one described in "llama.cpp に TurboQuant を実装 -- 2bit・
+ * 3bit の KV キャッシュ圧縮" (openalchemy.io):
+ *   - section "TurboQuant の何が違うのか": rotate before quantising, with a fast
+ *     Walsh-Hadamard transform (additions and subtractions only, self-inverse)
+ *     in place of a dense random rotation, then an optimal per-coordinate
+ *     Lloyd-Max scalar quantiser; the rotation is undone on read;
+ *   - section "どこまで小さくなるのか": a block is 128 values plus one FP16
+ *     norm (50 bytes for turbo3, 34 bytes for turbo2);
+ *   - section "実モデルでの数値": a head_dim of 128*m is m stacked blocks;
+ *   - section "現在の実装と、これから": the cache is stored compressed and
+ *     dequantised before attention today (tq_decode); the next step fuses the
+ *     dequantisation into the attention tiles so keys never exist in FP16
+ *     (tq_qk_scores).
+ *
+ * Block format (the page fixes only the byte counts; this layout is this
+ * library's convention):
+ *   - for a fp16 tensor [L, H, T, D] with D = 128*m, row (l, h, t) holds the m
+ *     blocks (l, h, t, j), j = 0..m-1, each 128 consecutive values;
+ *   - per block:  n = ||x||_2;  u = H x (unnormalised Sylvester-Hadamard
+ *     matrix, natural order, H H = 128 I);  t = u / n;
+ *     code_i = #{k : t_i >= tau_k}, tau the N(0,1) Lloyd-Max thresholds
+ *     (7 for turbo3, 3 for turbo2; a value on a threshold takes the upper
+ *     cell); a zero block gets every code = 2^bits / 2 and n = 0;
+ *   - decode: x_hat = (n16 / 128) * H * C[code], C the Lloyd-Max levels;
+ *   - a cache is two planes: codes u8 [L, H, Tc, m, 16*bits] (128 codes as one
+ *     little-endian bit stream, code i at bits [bits*i, bits*i + bits)) and
+ *     norms fp16 [L, H, Tc, m] (round to nearest even, saturating at 65504).
+ *     16*bits + 2 bytes per block: 50 (0.39 B/value) and 34 (0.27 B/value).
+ *
+ * Memory and streams: every pointer named "device" is device memory the
+ * caller owns (e.g. from torch on ROCm).  The library allocates, frees and
+ * synchronises nothing and keeps no per-call state.  stream is a hipStream_t
+ * passed as void* (NULL = the default stream); calls are asynchronous on it
+ * and their results are valid once the caller has synchronised that stream.
+ *
+ * Errors: arguments are checked on the host before any HIP call; a failed
+ * check returns a negative tq_status and launches nothing.  Work of size zero
+ * returns TQ_OK and launches nothing.  A launch that HIP reports as failed
+ * returns TQ_ERR_DEVICE.  Non-finite inputs are outside the contract: they do
+ * not fault, but their outputs are unspecified.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache types; the value is the number of bits per code. */
+enum tq_type { TQ_TURBO2 = 2, TQ_TURBO3 = 3 };
+
+enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_TYPE = -1,   /* type is not TQ_TURBO2 / TQ_TURBO3 */
+    TQ_ERR_SHAPE = -2,  /* negative size, D not a positive multiple of 128, Hq % Hkv, limits */
+    TQ_ERR_RANGE = -3,  /* t0 < 0 or t0 + T > Tc */
+    TQ_ERR_NULL = -4,   /* NULL pointer where there is work to do */
+    TQ_ERR_ALIGN = -5,  /* x / q / codes not 16-byte, norms not 2-byte, scores not 4-byte aligned */
+    TQ_ERR_ALIAS = -6,  /* an output range overlaps an input range or another output */
+    TQ_ERR_DEVICE = -7  /* HIP reported an error for the launch */
+};
+
+/* Largest head_dim tq_qk_scores accepts (16 blocks per vector). */
+#define TQ_QK_MAX_D 2048
+
+/* Bytes of packed codes per block: 48 (turbo3), 32 (turbo2); TQ_ERR_TYPE otherwise. */
+int tq_block_code_bytes(int type);
+/* Bytes per block including its fp16 norm: 50 (turbo3), 34 (turbo2); TQ_ERR_TYPE otherwise. */
+int tq_block_bytes(int type);
+/* Size of the codes plane of a [L, H, Tc, D] cache in bytes; negative tq_status on bad input. */
+int64_t tq_codes_nbytes(int type, int64_t L, int64_t H, int64_t Tc, int64_t D);
+/* Number of fp16 norms of a [L, H, Tc, D] cache; negative tq_status on bad input. */
+int64_t tq_norms_count(int64_t L, int64_t H, int64_t Tc, int64_t D);
+/* Static string naming a status code (never NULL). */
+const char *tq_status_string(int status);
+
+/* The float32 codebook the kernels use (host memory, computed by this library
+ * from the N(0,1) Lloyd-Max conditions): levels[2^type] ascending,
+ * thresholds[2^type - 1] (midpoints of adjacent levels).  Section
+ * "TurboQuant の何が違うのか" asks for the optimal Lloyd-Max codebook; the
+ * Gaussian is this library's reading.  Returns TQ_OK or TQ_ERR_TYPE/TQ_ERR_NULL. */
+int tq_codebook(int type, float *levels, float *thresholds);
+
+/* Encode (the cache write path: rotate + quantise + pack, section
+ * "TurboQuant の何が違うのか"; T = 1 is the per-token append of a decode step).
+ *   x      device fp16 [L, H, T, D], contiguous, 16-byte aligned (read only)
+ *   codes  device u8 [L, H, Tc, D/128, 16*type], 16-byte aligned
+ *   norms  device fp16 [L, H, Tc, D/128], 2-byte aligned
+ * Writes cache rows [t0, t0 + T) of every (l, h); other rows are untouched.
+ * Requires D % 128 == 0, 0 <= t0, t0 + T <= Tc, fewer than 2^31 blocks. */
+int tq_encode(int type, const void *x, int64_t L, int64_t H, int64_t T, int64_t D,
+              void *codes, void *norms, int64_t Tc, int64_t t0, void *stream);
+
+/* Decode (dequantise to fp16 before attention, section "現在の実装と、これから"):
+ *   codes, norms  device cache planes of a [L, H, Tc, D] cache (read only)
+ *   x             device fp16 [L, H, T, D], contiguous, 16-byte aligned
+ * Reads cache rows [t0, t0 + T) and writes x_hat rounded to fp16 (nearest even). */
+int tq_decode(int type, const void *codes, const void *norms, int64_t L, int64_t H,
+              int64_t Tc, int64_t D, int64_t t0, int64_t T, void *x, void *stream);
+
+/* Fused read of a compressed key cache (the fusion named in section
+ * "現在の実装と、これから": keys are never materialised in fp16):
+ *   k_codes, k_norms  device key cache of shape [B, Hkv, Tc, D] (read only)
+ *   q                 device fp16 [B, Hq, D], 16-byte aligned (read only)
+ *   scores            device fp32 [B, Hq, T], 4-byte aligned
+ * scores[b, h, t] = scale * sum_d q[b, h, d] * k_hat[b, h / G, t, d] for cache
+ * rows t in [0, T), G = Hq / Hkv (query heads h = g*G .. g*G + G - 1 share key
+ * head g), k_hat the decoded key kept in float (not rounded to fp16).
+ * Requires Hq % Hkv == 0, T <= Tc, D % 128 == 0 and D <= TQ_QK_MAX_D. */
+int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
+                 int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq, float scale,
+                 float *scores, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

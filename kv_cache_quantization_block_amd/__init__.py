@@ -1,0 +1,199 @@
+"""Python binding of libtq, the MI355X (gfx950) turbo3 / turbo2 KV-cache block codec.
+
+Argument marshalling only: every function forwards torch device pointers, sizes
+and the current HIP stream to the C ABI declared in ``include/tq.h``; all
+computation happens in the library's HIP kernels.  There is no CPU fallback:
+tensors must live on the GPU, and a missing ``libtq.so`` raises at import of
+the first call.
+
+Layouts (the library's block format):
+  x       fp16 [L, H, T, D], D = 128 * m, contiguous
+  codes   uint8 [L, H, Tc, m, 16 * type]   (type = 3 turbo3, 2 turbo2)
+  norms   fp16 [L, H, Tc, m]
+  q       fp16 [B, Hq, D];  scores fp32 [B, Hq, T]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "TQ_TURBO2", "TQ_TURBO3", "TQError", "lib", "lib_path", "header_functions",
+    "tq_block_code_bytes", "tq_block_bytes", "tq_codes_nbytes", "tq_norms_count",
+    "tq_status_string", "tq_codebook", "tq_encode", "tq_decode", "tq_qk_scores", "empty_cache",
+]
+
+TQ_TURBO2 = 2
+TQ_TURBO3 = 3
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libtq.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "tq.h")
+
+STATUS = {0: "TQ_OK", -1: "TQ_ERR_TYPE", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_RANGE",
+          -4: "TQ_ERR_NULL", -5: "TQ_ERR_ALIGN", -6: "TQ_ERR_ALIAS", -7: "TQ_ERR_DEVICE"}
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {tq_status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing; build it with "
+                           "`python -m kv_cache_quantization_block_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    L.tq_block_code_bytes.restype = i32
+    L.tq_block_code_bytes.argtypes = [i32]
+    L.tq_block_bytes.restype = i32
+    L.tq_block_bytes.argtypes = [i32]
+    L.tq_codes_nbytes.restype = i64
+    L.tq_codes_nbytes.argtypes = [i32, i64, i64, i64, i64]
+    L.tq_norms_count.restype = i64
+    L.tq_norms_count.argtypes = [i64, i64, i64, i64]
+    L.tq_status_string.restype = ctypes.c_char_p
+    L.tq_status_string.argtypes = [i32]
+    L.tq_codebook.restype = i32
+    L.tq_codebook.argtypes = [i32, vp, vp]
+    L.tq_encode.restype = i32
+    L.tq_encode.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp]
+    L.tq_decode.restype = i32
+    L.tq_decode.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp]
+    L.tq_qk_scores.restype = i32
+    L.tq_qk_scores.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp, vp]
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/tq.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)
+
+
+def tq_block_code_bytes(type: int) -> int:
+    return lib().tq_block_code_bytes(type)
+
+
+def tq_block_bytes(type: int) -> int:
+    return lib().tq_block_bytes(type)
+
+
+def tq_codes_nbytes(type: int, L: int, H: int, Tc: int, D: int) -> int:
+    return lib().tq_codes_nbytes(type, L, H, Tc, D)
+
+
+def tq_norms_count(L: int, H: int, Tc: int, D: int) -> int:
+    return lib().tq_norms_count(L, H, Tc, D)
+
+
+def tq_status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def tq_codebook(type: int):
+    """(levels, thresholds) float32 lists the kernels use."""
+    n = 1 << type
+    lv = (ctypes.c_float * n)()
+    th = (ctypes.c_float * (n - 1))()
+    rc = lib().tq_codebook(type, ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p))
+    if rc:
+        raise TQError(rc, "tq_codebook")
+    return list(lv), list(th)
+
+
+# ---------------------------------------------------------------- tensor calls
+
+def _stream(stream) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def empty_cache(type: int, L: int, H: int, Tc: int, D: int, device="cuda"):
+    """Uninitialised (codes, norms) planes of a [L, H, Tc, D] cache."""
+    if D % 128:
+        raise ValueError("D must be a multiple of 128")
+    m = D // 128
+    codes = torch.empty((L, H, Tc, m, 16 * type), dtype=torch.uint8, device=device)
+    norms = torch.empty((L, H, Tc, m), dtype=torch.float16, device=device)
+    return codes, norms
+
+
+def _cache_dims(codes: torch.Tensor, norms: torch.Tensor, type: int):
+    if codes.dim() != 5 or codes.shape[4] != 16 * type:
+        raise ValueError(f"codes must be [L, H, Tc, D/128, {16 * type}]")
+    L, H, Tc, m, _ = codes.shape
+    if tuple(norms.shape) != (L, H, Tc, m):
+        raise ValueError("norms must be [L, H, Tc, D/128]")
+    return L, H, Tc, m * 128
+
+
+def tq_encode(type: int, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
+              t0: int = 0, stream=None) -> None:
+    """Encode x [L, H, T, D] into cache rows [t0, t0 + T) (asynchronous)."""
+    L, H, Tc, D = _cache_dims(codes, norms, type)
+    if x.dim() != 4 or tuple(x.shape[:2]) != (L, H) or x.shape[3] != D:
+        raise ValueError("x must be [L, H, T, D] matching the cache")
+    T = x.shape[2]
+    rc = lib().tq_encode(type, _dev(x, "x", torch.float16), L, H, T, D,
+                         _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
+                         Tc, t0, _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_encode")
+
+
+def tq_decode(type: int, codes: torch.Tensor, norms: torch.Tensor, t0: int, x: torch.Tensor,
+              stream=None) -> None:
+    """Decode cache rows [t0, t0 + T) into x [L, H, T, D] fp16 (asynchronous)."""
+    L, H, Tc, D = _cache_dims(codes, norms, type)
+    if x.dim() != 4 or tuple(x.shape[:2]) != (L, H) or x.shape[3] != D:
+        raise ValueError("x must be [L, H, T, D] matching the cache")
+    T = x.shape[2]
+    rc = lib().tq_decode(type, _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
+                         L, H, Tc, D, t0, T, _dev(x, "x", torch.float16), _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_decode")
+
+
+def tq_qk_scores(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, q: torch.Tensor,
+                 scale: float, scores: torch.Tensor, stream=None) -> None:
+    """scores [B, Hq, T] = scale * q . k_hat over key-cache rows [0, T) (asynchronous)."""
+    B, Hkv, Tc, D = _cache_dims(k_codes, k_norms, type)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, Hq, D] matching the cache")
+    Hq = q.shape[1]
+    if scores.dim() != 3 or tuple(scores.shape[:2]) != (B, Hq):
+        raise ValueError("scores must be [B, Hq, T]")
+    T = scores.shape[2]
+    rc = lib().tq_qk_scores(type, _dev(k_codes, "k_codes", torch.uint8),
+                            _dev(k_norms, "k_norms", torch.float16), B, Hkv, Tc, D, T,
+                            _dev(q, "q", torch.float16), Hq, float(scale),
+                            _dev(scores, "scores", torch.float32), _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_qk_scores")

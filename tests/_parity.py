@@ -1,0 +1,88 @@
+"""Comparison rules between the HIP path and the CPU oracle (test helper).
+
+Rules (readings of the tolerances, each applied element by element):
+  codes   bit-exact, except values whose oracle t lies within TIE_BAND of a
+          decision threshold (both codes are then equally valid); every
+          mismatch must be such a tie and the mismatch fraction must not
+          exceed MISMATCH_FRAC (at least one mismatch is tolerated in samples
+          smaller than 1 / MISMATCH_FRAC values);
+  norms   fp16 bit-exact, or one ulp apart where the exact norm lies within
+          1e-6 (relative) of the midpoint of the two fp16 values (float32 on
+          the GPU vs binary64 in the oracle may round such a norm either way);
+  decode  |g - r| <= 1e-3 * max(|r|, 0.01 * rms(block of r)) + 2^-25, r the
+          oracle's binary64 decode of the GPU's own codes and norms (2^-25 is
+          half the smallest fp16 spacing: the output format's own resolution);
+  scores  |g - r| <= 2e-3 * max(|r|, 0.01 * ||q|| * ||k_hat||), r the oracle's
+          scores over the GPU-written cache.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TIE_BAND = 1e-5
+MISMATCH_FRAC = 1e-6
+
+
+def unpack_codes(codes, bits: int) -> np.ndarray:
+    """u8 [..., 16*bits] → int codes [..., 128] (little-endian bit stream)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    shp = codes.shape[:-1]
+    stream = np.unpackbits(codes.reshape(-1, 16 * bits), axis=1, bitorder="little")
+    c = (stream.reshape(-1, 128, bits) * (1 << np.arange(bits))).sum(axis=2)
+    return c.reshape(*shp, 128)
+
+
+def check_codes(bits, gpu_codes, ora_codes, ora_dist, what=""):
+    g = unpack_codes(gpu_codes, bits).reshape(-1)
+    o = unpack_codes(ora_codes, bits).reshape(-1)
+    d = np.asarray(ora_dist).reshape(-1)
+    assert g.shape == o.shape == d.shape
+    bad = g != o
+    nbad = int(bad.sum())
+    ties = int((d < TIE_BAND).sum())
+    if nbad:
+        assert np.all(d[bad] < TIE_BAND), \
+            f"{what}: {int((d[bad] >= TIE_BAND).sum())} code mismatches outside the tie band"
+        assert np.all(np.abs(g[bad] - o[bad]) == 1), f"{what}: mismatch by more than one cell"
+    allowed = max(1, int(MISMATCH_FRAC * g.size))
+    assert nbad <= allowed, f"{what}: {nbad} tie mismatches in {g.size} values (allowed {allowed})"
+    return {"values": int(g.size), "mismatches": nbad, "ties": ties}
+
+
+def check_norms(gpu_n16, ora_n16, x_blocks, what=""):
+    g = np.asarray(gpu_n16, dtype=np.float16).reshape(-1)
+    o = np.asarray(ora_n16, dtype=np.float16).reshape(-1)
+    diff = g.view(np.uint16) != o.view(np.uint16)
+    n = int(diff.sum())
+    if n:
+        x = np.asarray(x_blocks, dtype=np.float16).reshape(-1, 128)[diff].astype(np.float64)
+        exact = np.linalg.norm(x, axis=1)
+        gi, oi = g[diff].view(np.uint16).astype(np.int64), o[diff].view(np.uint16).astype(np.int64)
+        assert np.all(np.abs(gi - oi) == 1), f"{what}: norm differs by more than one ulp"
+        mid = (g[diff].astype(np.float64) + o[diff].astype(np.float64)) / 2
+        assert np.all(np.abs(exact - mid) <= 1e-6 * exact), f"{what}: norm ulp diff away from a midpoint"
+    return {"norm_ulp_diffs": n}
+
+
+def check_decode(gpu_x16, ref, what=""):
+    g = np.asarray(gpu_x16, dtype=np.float16).astype(np.float64).reshape(-1, 128)
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, 128)
+    rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+    tol = 1e-3 * np.maximum(np.abs(r), 0.01 * rms) + 2.0 ** -25
+    err = np.abs(g - r)
+    worst = float(np.max(err / tol)) if err.size else 0.0
+    assert np.all(err <= tol), f"{what}: decode error {worst:.3f} x tolerance"
+    nz = np.abs(r) > 0
+    max_rel = float(np.max(err[nz] / np.abs(r[nz]))) if nz.any() else 0.0
+    return {"decode_worst_over_tol": worst, "decode_max_rel": max_rel}
+
+
+def check_scores(gpu, ref, qnorm, knorm, what=""):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    floor = 0.01 * np.asarray(qnorm) * np.asarray(knorm)
+    tol = 2e-3 * np.maximum(np.abs(r), floor)
+    err = np.abs(g - r)
+    worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    assert np.all(err <= tol), f"{what}: score error {worst:.3f} x tolerance"
+    return {"scores_worst_over_tol": worst}

@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, sizes
+its planes as the article prints, rejects bad arguments before touching HIP,
+and carries float32 codebooks equal to the oracle's binary64 solution rounded
+to float.  No compute call runs here (no GPU)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_block_amd as tq
+import oracle
+
+OK, E_TYPE, E_SHAPE, E_RANGE, E_NULL, E_ALIGN, E_ALIAS = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tq.lib_path):
+        from kv_cache_quantization_block_amd import build
+        build.build()
+    return tq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = tq.header_functions()
+    assert {"tq_encode", "tq_decode", "tq_qk_scores", "tq_codebook"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_sizes():
+    """Section "どこまで小さくなるのか": 128 values + one fp16 norm = 50 / 34 bytes."""
+    assert tq.tq_block_code_bytes(3) == 48 and tq.tq_block_bytes(3) == 50
+    assert tq.tq_block_code_bytes(2) == 32 and tq.tq_block_bytes(2) == 34
+    assert tq.tq_block_bytes(4) == E_TYPE and tq.tq_block_code_bytes(1) == E_TYPE
+    assert tq.tq_codes_nbytes(3, 48, 8, 32768, 128) == 48 * 8 * 32768 * 48
+    assert tq.tq_codes_nbytes(2, 32, 4, 32768, 256) == 32 * 4 * 32768 * 2 * 32
+    assert tq.tq_norms_count(32, 4, 32768, 256) == 32 * 4 * 32768 * 2
+    assert tq.tq_codes_nbytes(3, 1, 1, 1, 100) == E_SHAPE
+    assert tq.tq_norms_count(1, 1, 1, 0) == E_SHAPE
+    assert tq.tq_codes_nbytes(3, 1 << 40, 1 << 40, 1, 128) == E_SHAPE   # overflow
+
+
+def test_status_strings():
+    for code, name in tq.STATUS.items():
+        assert tq.tq_status_string(code).startswith(name)
+    assert "unknown" in tq.tq_status_string(12345)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_codebook_is_oracle_solution_rounded_to_float(bits):
+    """The library solves the Lloyd-Max conditions on its own; its float32 levels and
+    thresholds must equal float32(oracle's binary64 solution)."""
+    lv, th = tq.tq_codebook(bits)
+    olv, oth, _ = oracle.codebook(bits)
+    assert np.array_equal(np.array(lv, np.float32), olv.astype(np.float32))
+    assert np.array_equal(np.array(th, np.float32), oth.astype(np.float32))
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+# Fake, never dereferenced device addresses: validation must reject before any HIP call.
+X, C, N, Q, S = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def test_encode_validation(L):
+    e = L.tq_encode
+    assert e(4, _p(X), 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_TYPE
+    assert e(3, _p(X), 1, 1, 1, 100, _p(C), _p(N), 1, 0, None) == E_SHAPE
+    assert e(3, _p(X), 1, 1, 1, 0, _p(C), _p(N), 1, 0, None) == E_SHAPE
+    assert e(3, _p(X), -1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_SHAPE
+    assert e(3, _p(X), 1, 1, 2, 128, _p(C), _p(N), 4, 3, None) == E_RANGE
+    assert e(3, _p(X), 1, 1, 1, 128, _p(C), _p(N), 4, -1, None) == E_RANGE
+    assert e(3, _p(X), 1, 1, 5, 128, _p(C), _p(N), 4, 0, None) == E_RANGE
+    assert e(3, None, 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_NULL
+    assert e(3, _p(X), 1, 1, 1, 128, None, _p(N), 1, 0, None) == E_NULL
+    assert e(3, _p(X + 8), 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_ALIGN
+    assert e(3, _p(X), 1, 1, 1, 128, _p(C + 4), _p(N), 1, 0, None) == E_ALIGN
+    assert e(3, _p(X), 1, 1, 1, 128, _p(C), _p(N + 1), 1, 0, None) == E_ALIGN
+    assert e(3, _p(X), 1, 1, 1, 128, _p(X + 128), _p(N), 1, 0, None) == E_ALIAS
+    assert e(3, _p(X), 1, 1, 1, 128, _p(C), _p(C + 16), 1, 0, None) == E_ALIAS
+    assert e(3, _p(X), 2, 3, 4, 256, _p(C), _p(X + 2 * 3 * 4 * 256 * 2 - 2), 9, 0, None) == E_ALIAS
+    # zero work is a no-op success even with null pointers
+    assert e(3, None, 0, 8, 16, 128, None, None, 16, 0, None) == OK
+    assert e(2, None, 1, 1, 0, 128, None, None, 8, 8, None) == OK
+
+
+def test_decode_validation(L):
+    d = L.tq_decode
+    assert d(1, _p(C), _p(N), 1, 1, 1, 128, 0, 1, _p(X), None) == E_TYPE
+    assert d(3, _p(C), _p(N), 1, 1, 1, 129, 0, 1, _p(X), None) == E_SHAPE
+    assert d(3, _p(C), _p(N), 1, 1, 4, 128, 2, 3, _p(X), None) == E_RANGE
+    assert d(3, _p(C), None, 1, 1, 1, 128, 0, 1, _p(X), None) == E_NULL
+    assert d(3, _p(C), _p(N), 1, 1, 1, 128, 0, 1, _p(X + 2), None) == E_ALIGN
+    assert d(3, _p(C), _p(N), 1, 1, 1, 128, 0, 1, _p(C), None) == E_ALIAS
+    assert d(3, None, None, 1, 1, 5, 128, 5, 0, None, None) == OK
+
+
+def test_qk_validation(L):
+    f = L.tq_qk_scores
+    S4 = ctypes.cast(ctypes.c_void_p(S), ctypes.POINTER(ctypes.c_float))
+    args = lambda **kw: dict(dict(t=3, c=_p(C), n=_p(N), B=1, Hkv=2, Tc=8, D=128, T=8, q=_p(Q),
+                                  Hq=8, s=ctypes.c_float(1.0), o=S4), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["t"], a["c"], a["n"], a["B"], a["Hkv"], a["Tc"], a["D"], a["T"], a["q"],
+                 a["Hq"], a["s"], a["o"], None)
+
+    assert call(t=5) == E_TYPE
+    assert call(Hq=7) == E_SHAPE
+    assert call(Hkv=0) == E_SHAPE
+    assert call(D=192) == E_SHAPE
+    assert call(D=4096) == E_SHAPE
+    assert call(T=9) == E_RANGE
+    assert call(q=None) == E_NULL
+    assert call(q=_p(Q + 2)) == E_ALIGN
+    assert call(o=ctypes.cast(ctypes.c_void_p(S + 2), ctypes.POINTER(ctypes.c_float))) == E_ALIGN
+    assert call(o=ctypes.cast(ctypes.c_void_p(Q), ctypes.POINTER(ctypes.c_float))) == E_ALIAS
+    assert call(B=0, c=None, n=None, q=None) == OK
+    assert call(T=0) == OK
+
+
+def test_codebook_validation(L):
+    buf = (ctypes.c_float * 8)()
+    assert L.tq_codebook(4, buf, buf) == E_TYPE
+    assert L.tq_codebook(3, None, buf) == E_NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 1, 4, 128), dtype=torch.float16)
+    codes = torch.zeros((1, 1, 4, 1, 48), dtype=torch.uint8)
+    norms = torch.zeros((1, 1, 4, 1), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tq.tq_encode(3, x, codes, norms)

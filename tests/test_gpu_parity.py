@@ -1,0 +1,183 @@
+"""HIP path vs the CPU oracle on small inputs (GPU).
+
+Every case feeds the same fp16 bytes to the library (through the C ABI via the
+Python binding) and to the oracle, then compares element by element under the
+rules in _parity.py.  Sizes span several 64-block wave tiles with ragged tails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import kv_cache_quantization_block_amd as tq
+import oracle
+from _parity import check_codes, check_decode, check_norms, check_scores, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+SENT_CODE = 0xA5
+SENT_NORM = 7.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    tq.lib()
+
+
+def _rand_kv(seed, L, H, T, D, n_out=3, row_scale=True, t3=False):
+    spec = gen.KVSpec(n_outliers=n_out, row_scale=row_scale, student_t3=t3)
+    return gen.kv_tensor(seed, "K", spec, L, H, T, D)
+
+
+def _gpu_encode(bits, x, Tc, t0):
+    L, H, T, D = x.shape
+    codes, norms = tq.empty_cache(bits, L, H, Tc, D)
+    codes.fill_(SENT_CODE)
+    norms.fill_(SENT_NORM)
+    tq.tq_encode(bits, x.cuda(), codes, norms, t0)
+    return codes, norms
+
+
+def _check_roundtrip(bits, x, Tc, t0, what):
+    """Encode on both sides, compare the written rows, untouched rows, then decode."""
+    L, H, T, D = x.shape
+    m = D // 128
+    codes, norms = _gpu_encode(bits, x, Tc, t0)
+    out = torch.empty((L, H, T, D), dtype=torch.float16, device="cuda")
+    tq.tq_decode(bits, codes, norms, t0, out)
+    torch.cuda.synchronize()
+    gc, gn, gx = codes.cpu().numpy(), norms.cpu().numpy(), out.cpu().numpy()
+
+    xn = x.numpy()
+    oc = np.full(gc.shape, SENT_CODE, np.uint8)
+    on = np.full(gn.shape, SENT_NORM, np.float16)
+    dist = oracle.encode(bits, xn, oc, on, t0=t0, want_dist=True)
+    rows = slice(t0, t0 + T)
+    st = check_codes(bits, gc[:, :, rows], oc[:, :, rows], dist.reshape(L, H, T, m, 128), what)
+    st.update(check_norms(gn[:, :, rows], on[:, :, rows], xn, what))
+    # rows outside [t0, t0+T) untouched
+    assert np.all(gc[:, :, :t0] == SENT_CODE) and np.all(gc[:, :, t0 + T:] == SENT_CODE)
+    assert np.all(gn[:, :, :t0] == SENT_NORM) and np.all(gn[:, :, t0 + T:] == SENT_NORM)
+    # decode of the GPU's own cache vs the oracle's binary64 decode of it
+    ref, _ = oracle.decode(bits, gc, gn, t0, T)
+    st.update(check_decode(gx, ref, what))
+    return st
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_single_head_workload(bits):
+    """1 x 1 x 1024 x 128, N(0,1) with 4 fixed x20 outlier channels (1024 blocks)."""
+    w = gen.WORKLOADS["single_head"]
+    x = gen.kv_tensor(w.seed, "K", w.spec, w.L, w.H, w.T, w.D)
+    st = _check_roundtrip(bits, x, w.T, 0, "single_head")
+    print(st)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("shape", [
+    (2, 3, 37, 128, 50, 5),     # 222 blocks: ragged last tile, t0 > 0
+    (1, 2, 65, 256, 65, 0),     # head_dim 256, odd T
+    (3, 1, 1, 128, 9, 8),       # single-token append at the last row
+    (1, 1, 64, 384, 70, 6),     # three blocks per row
+    (2, 2, 300, 128, 300, 0),   # several tiles per (l, h)
+])
+def test_ragged_shapes(bits, shape):
+    L, H, T, D, Tc, t0 = shape
+    x = _rand_kv(11 + T + D, L, H, T, D)
+    _check_roundtrip(bits, x, Tc, t0, f"shape {shape}")
+
+
+def _special_blocks():
+    rows = []
+    z = np.zeros(128, np.float32)
+    rows.append(z.copy())                               # zero block
+    rows.append(-z)                                     # -0.0 block
+    for j, a in ((0, 1.0), (5, -2.0), (127, 0.5), (64, 300.0)):
+        r = z.copy(); r[j] = a; rows.append(r)         # one-hots
+    r = z.copy(); r[0] = r[1] = 1.0; rows.append(r)    # exact zero ties
+    rows.append(np.ones(128, np.float32))               # constant
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(128)] for i in range(128)], np.float32)
+    rows.append(H[37] * 3.0)                             # a Hadamard row
+    rows.append(np.full(128, 65504.0, np.float32))      # saturating norm
+    rows.append(np.full(128, 2.0 ** -24, np.float32))   # subnormal values
+    r = np.random.default_rng(0).standard_normal(128).astype(np.float32) * 1e-3
+    r[3] = 60000.0; rows.append(r)                      # one huge outlier
+    return np.stack(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_special_blocks_bit_exact(bits):
+    """Zero / -0 blocks, one-hots, exact-zero ties, saturating and subnormal norms:
+    every code and norm must equal the oracle's exactly (these t are exact in float)."""
+    xb = _special_blocks()
+    nb = xb.shape[0]
+    x = torch.from_numpy(xb).reshape(1, 1, nb, 128)
+    codes, norms = _gpu_encode(bits, x, nb, 0)
+    out = torch.empty((1, 1, nb, 128), dtype=torch.float16, device="cuda")
+    tq.tq_decode(bits, codes, norms, 0, out)
+    torch.cuda.synchronize()
+    oc, on, _ = oracle.encode_blocks(bits, xb)
+    gc = codes.cpu().numpy().reshape(nb, -1)
+    gn = norms.cpu().numpy().reshape(nb)
+    assert np.array_equal(unpack_codes(gc, bits), unpack_codes(oc, bits))
+    assert np.array_equal(gn.view(np.uint16), on.view(np.uint16))
+    assert float(gn[-3]) == 65504.0
+    ref, _ = oracle.decode_blocks(bits, gc, gn)
+    check_decode(out.cpu().numpy(), ref, "special")
+    assert np.all(out.cpu().numpy().reshape(nb, 128)[:2] == 0)   # zero blocks decode to 0
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_append_leaves_other_rows(bits):
+    """Decode-step append: one token per (layer, head) written at row t0; every other
+    byte of the cache is unchanged."""
+    L, H, Tc, D = 2, 4, 33, 128
+    prefill = _rand_kv(21, L, H, Tc - 1, D)
+    codes, norms = tq.empty_cache(bits, L, H, Tc, D)
+    codes.zero_()
+    norms.zero_()
+    tq.tq_encode(bits, prefill.cuda(), codes, norms, 0)
+    before_c, before_n = codes.clone(), norms.clone()
+    tok = _rand_kv(22, L, H, 1, D)
+    tq.tq_encode(bits, tok.cuda(), codes, norms, Tc - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(codes[:, :, :Tc - 1], before_c[:, :, :Tc - 1])
+    assert torch.equal(norms[:, :, :Tc - 1], before_n[:, :, :Tc - 1])
+    oc, on, dist = oracle.encode_blocks(bits, tok.numpy(), want_dist=True)
+    check_codes(bits, codes[:, :, Tc - 1].cpu().numpy().reshape(-1, 16 * bits), oc, dist, "append")
+    check_norms(norms[:, :, Tc - 1].cpu().numpy(), on, tok.numpy(), "append")
+
+
+def _qk_case(bits, B, Hkv, G, Tc, T, D, seed):
+    k = _rand_kv(seed, B, Hkv, Tc, D)
+    codes, norms = _gpu_encode(bits, k, Tc, 0)
+    q = gen.queries(seed + 1, B, Hkv * G, D)
+    scale = 1.0 / math.sqrt(D)
+    scores = torch.empty((B, Hkv * G, T), dtype=torch.float32, device="cuda")
+    tq.tq_qk_scores(bits, codes, norms, q.cuda(), scale, scores)
+    torch.cuda.synchronize()
+    gc, gn = codes.cpu().numpy(), norms.cpu().numpy()
+    ref = oracle.qk_scores(bits, gc, gn, q.numpy(), scale, T=T)
+    khat, _ = oracle.decode(bits, gc, gn, 0, T)                       # [B, Hkv, T, D]
+    kn = np.linalg.norm(khat, axis=-1)                                  # [B, Hkv, T]
+    qn = np.linalg.norm(q.numpy().astype(np.float64), axis=-1)         # [B, Hq]
+    knh = np.repeat(kn, G, axis=1)                                      # head h reads kv h // G
+    return check_scores(scores.cpu().numpy(), ref, qn[:, :, None] * scale, knh,
+                        f"qk bits={bits} B={B} Hkv={Hkv} G={G} T={T} D={D}")
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("case", [
+    (2, 2, 4, 100, 97, 128),     # GQA group 4, ragged T < Tc
+    (1, 3, 1, 70, 70, 128),      # no grouping
+    (2, 1, 8, 40, 33, 128),      # group 8: two passes of four heads
+    (1, 2, 3, 50, 50, 256),      # odd group, head_dim 256
+    (1, 1, 2, 1100, 1100, 384),  # three blocks per row (lanes padded to 16), two token chunks
+    (1, 2, 5, 20, 17, 1024),     # eight blocks per row
+])
+def test_qk_scores(bits, case):
+    B, Hkv, G, Tc, T, D = case
+    print(_qk_case(bits, B, Hkv, G, Tc, T, D, seed=31 + D + G))
