@@ -33,6 +33,7 @@
 // at compile time.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "internal.h"
 
@@ -106,143 +107,269 @@ __device__ __forceinline__ int64_t cache_block(uint32_t b, uint32_t row_blocks,
     return (int64_t)lh * cache_row_blocks + t0_blocks + r;
 }
 
+// Wave tiles: tile i is x-blocks [64 i, 64 i + 64) (the last one may be short).
+// Encode and decode run persistent waves: wave w handles tiles w, w + W, w + 2W...
+// (W = waves in the grid), prefetching tile i + W while it computes tile i, so
+// HBM traffic and VALU work of different tiles overlap inside every wave.
+
 // ---------------------------------------------------------------- encode
+//
+// Two lanes per block: lane l holds half h = l / 32 (values 64 h .. 64 h + 63) of
+// block l % 32 of a 32-block (8 KB) wave tile.  The butterfly stages of spans 1..32
+// run inside each lane; the span-64 stage pairs the two halves: one
+// v_permlane32_swap per two registers brings value i of the partner next to value
+// i of this lane, after which the butterfly is again in-lane.  A lane then owns the
+// outputs of positions [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h), i.e. two
+// 32-code groups that are whole 12-byte (turbo3) / 8-byte (turbo2) runs of the
+// packed block, so no code ever crosses lanes.  64 floats per lane keep a wave
+// under 168 VGPRs: three waves per SIMD, each with the next tile in flight.
+
+constexpr int kEncTileBlocks = 32;
+constexpr int kEncTileBytes = kEncTileBlocks * kBlock * 2;   // 8 KB of fp16
+
+// R[k] = chunk (lane % 16) of block 4 k + lane / 16 of the tile; zeros past nb.
+__device__ __forceinline__ void load_enc_tile(u4_t (&R)[8], const uint8_t *__restrict__ x,
+                                              uint32_t b0, uint32_t nb, uint32_t lane)
+{
+    const uint8_t *src = x + (size_t)b0 * (kBlock * 2) + lane * 16;
+    if (nb == kEncTileBlocks) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            R[k] = *(const u4_t *)(src + k * 1024);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            R[k] = 4 * k + (lane >> 4) < nb ? *(const u4_t *)(src + k * 1024) : u4_t{0, 0, 0, 0};
+    }
+}
+
+// (upper 32 lanes of a) <-> (lower 32 lanes of b), returned as the new (a, b).
+__device__ __forceinline__ void swap32(float &a, float &b)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                              __builtin_bit_cast(uint32_t, b), false, false);
+    const uint32_t r0 = r[0], r1 = r[1];   // through scalars: see as_h2
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
 
 template <int BITS>
-__global__ __launch_bounds__(256, 2) void encode_kernel(const uint8_t *__restrict__ x,
-                                                     uint32_t nblocks, uint32_t row_blocks,
-                                                     int64_t cache_row_blocks, int64_t t0_blocks,
-                                                     uint8_t *__restrict__ codes,
-                                                     uint16_t *__restrict__ norms, Codebook cb)
+__global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restrict__ x,
+                                                        uint32_t nblocks, uint32_t row_blocks,
+                                                        int64_t cache_row_blocks,
+                                                        int64_t t0_blocks,
+                                                        uint8_t *__restrict__ codes,
+                                                        uint16_t *__restrict__ norms, Codebook cb)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile_all[kWavesPerGroup][kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_all[kWavesPerGroup][kEncTileBytes];
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t b0 = (blockIdx.x * kWavesPerGroup + wave) * kBlocksPerWave;
-    if (b0 >= nblocks)
+    const uint32_t blk = lane & 31u, half = lane >> 5;
+    const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
+    const uint32_t stride = gridDim.x * kWavesPerGroup;
+    uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
+    if (tile >= ntiles)
         return;
-    uint8_t *tile = tile_all[wave];
-    const uint32_t nb = min(nblocks - b0, (uint32_t)kBlocksPerWave);
+    uint8_t *lds = tile_all[wave];
+    constexpr int GW = BITS;              // 32-bit words per 32-code group
+    constexpr int GB = 4 * BITS;          // bytes per 32-code group
+    constexpr int CB = 16 * BITS;         // code bytes per block
+    constexpr float mid = (float)(1 << (BITS - 1));
 
-    // 1. coalesced 16-byte loads of the wave's 64 blocks, transposed through LDS
-    {
-        const uint8_t *src = x + (size_t)b0 * (kBlock * 2);
-        u4_t r[16];
-        if (nb == kBlocksPerWave) {   // full tile (wave-uniform): no per-load guard
+    u4_t R[8];
+    load_enc_tile(R, x, tile * kEncTileBlocks, min(nblocks - tile * kEncTileBlocks, 32u), lane);
+    for (;;) {
+        const uint32_t b0 = tile * kEncTileBlocks;
+        const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
+
+        // 1. park the tile in LDS (XOR-swizzled), then prefetch the next one into R
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                r[k] = *(const u4_t *)(src + k * 1024 + lane * 16);
-        } else {
+        for (int k = 0; k < 8; ++k)
+            *(u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)) = R[k];
+        wave_lds_sync();
+        const uint32_t next = tile + stride;
+        if (next < ntiles)
+            load_enc_tile(R, x, next * kEncTileBlocks,
+                          min(nblocks - next * kEncTileBlocks, (uint32_t)kEncTileBlocks), lane);
+
+        // 2. this lane's half block: 64 fp16 values as 32 pairs
+        h2_t v[32];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                uint32_t blk = 4 * k + (lane >> 4);
-                r[k] = blk < nb ? *(const u4_t *)(src + k * 1024 + lane * 16) : u4_t{0, 0, 0, 0};
+        for (int c = 0; c < 8; ++c) {
+            const u4_t wv = *(const u4_t *)(lds + swz(blk, 8 * half + c));
+            v[4 * c + 0] = as_h2(wv.x);
+            v[4 * c + 1] = as_h2(wv.y);
+            v[4 * c + 2] = as_h2(wv.z);
+            v[4 * c + 3] = as_h2(wv.w);
+        }
+        wave_lds_sync();   // the tile area is reused below for the packed codes
+
+        // 3. rotation, with the norm's sum of squares (exact fp16 squares, four
+        //    partial sums) taken from the same pairs.  Spans 1 and 2 come straight
+        //    from the fp16 pairs; the results at positions with bit 1 set come out
+        //    negated (p - (x0 + x1) instead of (x0 + x1) - p), and every later stage
+        //    only combines positions that agree in bit 1, so u[r] ends as -(H x)
+        //    wherever r & 2 (exact negations).
+        float u[64];
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            const h2_t pm = {(_Float16)1.0f, (_Float16)-1.0f};
+            const h2_t mm = {(_Float16)-1.0f, (_Float16)-1.0f};
+            const h2_t mp = {(_Float16)-1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                acc[(2 * g) & 3] = __builtin_amdgcn_fdot2(v[2 * g], v[2 * g], acc[(2 * g) & 3], false);
+                acc[(2 * g + 1) & 3] =
+                    __builtin_amdgcn_fdot2(v[2 * g + 1], v[2 * g + 1], acc[(2 * g + 1) & 3], false);
+                const float p = dot2(v[2 * g + 1], one);   //  x2 + x3
+                const float q = dot2(v[2 * g + 1], pm);    //  x2 - x3
+                u[4 * g + 0] = dot2(v[2 * g], one, p);     //  (x0 + x1) + (x2 + x3)
+                u[4 * g + 1] = dot2(v[2 * g], pm, q);      //  (x0 - x1) + (x2 - x3)
+                u[4 * g + 2] = dot2(v[2 * g], mm, p);      // -((x0 + x1) - (x2 + x3))
+                u[4 * g + 3] = dot2(v[2 * g], mp, q);      // -((x0 - x1) - (x2 - x3))
             }
         }
+        float ssh = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        float sso = ssh;
+        swap32(ssh, sso);   // low lanes: sso = partner's sum; high lanes: ssh = partner's sum
+        const float ss = half ? (sso + ssh) : (ssh + sso);   // same order in both lanes
+        const float n = __builtin_sqrtf(ss);
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-            *(u4_t *)(tile + swz(4 * k + (lane >> 4), lane & 15u)) = r[k];
-    }
-    wave_lds_sync();
-    h2_t v[64];
+        for (int h = 4; h < 64; h <<= 1)
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const u4_t w = *(const u4_t *)(tile + swz(lane, c));
-        v[4 * c + 0] = as_h2(w.x);
-        v[4 * c + 1] = as_h2(w.y);
-        v[4 * c + 2] = as_h2(w.z);
-        v[4 * c + 3] = as_h2(w.w);
-    }
-
-    // 2. norm: sum of squares with exact fp16 products, eight partial sums
-    float acc[8];
+            for (int i = 0; i < 64; i += 2 * h)
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        acc[k] = 0.0f;
+                for (int j = i; j < i + h; ++j) {
+                    const float a = u[j], b = u[j + h];
+                    u[j] = a + b;
+                    u[j + h] = a - b;
+                }
+        // span 64 across the two halves: after the swap, the low lane holds positions
+        // (i, 64 + i) and the high lane (32 + i, 96 + i) in (u[i], u[i + 32])
 #pragma unroll
-    for (int k = 0; k < 64; ++k)
-        acc[k & 7] = __builtin_amdgcn_fdot2(v[k], v[k], acc[k & 7], false);
-    const float ss = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    const float n = __builtin_sqrtf(ss);
-
-    // 3. rotation.  Stages of span 1 and 2 straight from the fp16 pairs, two
-    //    results per input pair; the results at positions with bit 1 set come out
-    //    negated (p - (x0 + x1) instead of (x0 + x1) - p), which saves the negation.
-    //    Every later stage only combines positions that agree in bit 1, so after the
-    //    remaining stages u[i] holds -(H x)[i] exactly wherever i & 2, and +(H x)[i]
-    //    elsewhere (IEEE rounding is symmetric, the values are exact negations).
-    float u[kBlock];
-    {
-        const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-        const h2_t pm = {(_Float16)1.0f, (_Float16)-1.0f};
-        const h2_t mm = {(_Float16)-1.0f, (_Float16)-1.0f};
-        const h2_t mp = {(_Float16)-1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int g = 0; g < 32; ++g) {
-            const float p = dot2(v[2 * g + 1], one);          //  x2 + x3
-            const float q = dot2(v[2 * g + 1], pm);           //  x2 - x3
-            u[4 * g + 0] = dot2(v[2 * g], one, p);            //  (x0 + x1) + (x2 + x3)
-            u[4 * g + 1] = dot2(v[2 * g], pm, q);             //  (x0 - x1) + (x2 - x3)
-            u[4 * g + 2] = dot2(v[2 * g], mm, p);             // -((x0 + x1) - (x2 + x3))
-            u[4 * g + 3] = dot2(v[2 * g], mp, q);             // -((x0 - x1) - (x2 - x3))
+        for (int i = 0; i < 32; ++i) {
+            swap32(u[i], u[i + 32]);
+            const float a = u[i], b = u[i + 32];
+            u[i] = a + b;
+            u[i + 32] = a - b;
         }
-    }
-    fwht_from<4>(u);
 
-    // 4. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F).  The
-    //    polynomial's coefficients absorb 1/n and the clamp is scaled by n, so the
-    //    division is never done per value; g is odd, so a negated u[i] is handled
-    //    by negating the last product (bit-identical to quantising +(H x)[i]).
-    //    n == 0 (zero block) gives F = 2^b/2 for every value.
-    const float rn = n > 0.0f ? 1.0f / n : 0.0f;
-    const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
-    const float hi = cb.clamp_t * n, lo = -hi;
-    constexpr float mid = (float)(1 << (BITS - 1));
-    constexpr int NW = 4 * BITS;   // 32-bit words of packed codes per block
-    uint32_t w[NW];
+        // 5. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F); the
+        //    coefficients absorb 1/n and the clamp is scaled by n, so no division per
+        //    value; g is odd, so a negated u[r] negates the last product.  n == 0
+        //    (zero block) gives F = 2^b/2 for every value.
+        const float rn = n > 0.0f ? __builtin_amdgcn_rcpf(n) : 0.0f;
+        const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
+        const float hi = cb.clamp_t * n, lo = -hi;
+        uint32_t wa[GW], wb[GW];   // groups r in [0, 32) and [32, 64)
 #pragma unroll
-    for (int k = 0; k < NW; ++k)
-        w[k] = 0u;
+        for (int k = 0; k < GW; ++k)
+            wa[k] = wb[k] = 0u;
 #pragma unroll
-    for (int i = 0; i < kBlock; ++i) {
-        const float uc = __builtin_amdgcn_fmed3f(u[i], lo, hi);
-        const float ui = (i & 2) ? -uc : uc;
-        float F;
-        if constexpr (BITS == 3) {
-            // g(t) = t * (g1 + g2 |t| + g3 t^2)
-            float p = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
-            p = __builtin_fmaf(__builtin_fabsf(uc), p, k1);
-            F = __builtin_fmaf(ui, p, mid);
-        } else {
-            F = __builtin_fmaf(ui, k1, mid);
+        for (int r = 0; r < 64; ++r) {
+            const float uc = __builtin_amdgcn_fmed3f(u[r], lo, hi);
+            const float ui = (r & 2) ? -uc : uc;
+            float F;
+            if constexpr (BITS == 3) {
+                // g(t) = t * (g1 + g2 |t| + g3 t^2)
+                float p = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
+                p = __builtin_fmaf(__builtin_fabsf(uc), p, k1);
+                F = __builtin_fmaf(ui, p, mid);
+            } else {
+                F = __builtin_fmaf(ui, k1, mid);
+            }
+            const uint32_t code = (uint32_t)F;
+            const int i = r & 31, bit = BITS * i, wi = bit >> 5, sh = bit & 31;
+            uint32_t *w = r < 32 ? wa : wb;
+            w[wi] |= code << sh;
+            if (sh + BITS > 32)
+                w[wi + 1] |= code >> (32 - sh);
         }
-        const uint32_t code = (uint32_t)F;
-        const int bit = BITS * i, wi = bit >> 5, sh = bit & 31;
-        w[wi] |= code << sh;
-        if (sh + BITS > 32)
-            w[wi + 1] |= code >> (32 - sh);
-    }
+        const uint16_t n16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf(n, 65504.0f));
 
-    // 5. store codes (16*BITS bytes) and the fp16 norm of this lane's block
-    const uint32_t b = b0 + lane;
-    if (b < nblocks) {
-        const int64_t dst = cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
-        u4_t *out = (u4_t *)(codes + dst * (16 * BITS));
+        // 6. store.  Consecutive cache blocks (always, unless the tile straddles two
+        //    (layer, head) rows of a cache longer than x): stage the tile's codes in
+        //    LDS and write them as contiguous 16-byte stores.
+        const int64_t dst0 = cache_block(b0, row_blocks, cache_row_blocks, t0_blocks);
+        const int64_t dstl = cache_block(b0 + nb - 1, row_blocks, cache_row_blocks, t0_blocks);
+        const bool live = blk < nb;
+        if (dstl - dst0 == (int64_t)nb - 1) {
+            uint32_t *st = (uint32_t *)(lds + blk * CB + GB * half);
 #pragma unroll
-        for (int k = 0; k < BITS; ++k)
-            out[k] = u4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
-        const _Float16 n16 = (_Float16)__builtin_fminf(n, 65504.0f);
-        norms[dst] = __builtin_bit_cast(uint16_t, n16);
+            for (int k = 0; k < GW; ++k) {
+                st[k] = wa[k];
+                st[2 * GW + k] = wb[k];
+            }
+            wave_lds_sync();
+            uint8_t *gdst = codes + dst0 * CB;
+            const uint32_t nchunks = nb * BITS;   // 16-byte chunks of the tile's codes
+#pragma unroll
+            for (int k = 0; k < (2 * BITS + 3) / 4; ++k) {
+                const uint32_t c = k * 64 + lane;
+                if (c < 2u * BITS * 16u) {
+                    const u4_t val = *(const u4_t *)(lds + c * 16);
+                    if (c < nchunks)
+                        *(u4_t *)(gdst + c * 16) = val;
+                }
+            }
+            if (live && half == 0)
+                norms[dst0 + blk] = n16;
+        } else if (live) {
+            const int64_t dst = cache_block(b0 + blk, row_blocks, cache_row_blocks, t0_blocks);
+            uint32_t *out = (uint32_t *)(codes + dst * CB + GB * half);
+#pragma unroll
+            for (int k = 0; k < GW; ++k) {
+                out[k] = wa[k];
+                out[2 * GW + k] = wb[k];
+            }
+            if (half == 0)
+                norms[dst] = n16;
+        }
+
+        tile = next;
+        if (tile >= ntiles)
+            break;
+        wave_lds_sync();   // the staged codes are read before the next tile lands
     }
 }
 
 // ---------------------------------------------------------------- decode
 
+// This lane's block of the cache: packed codes and the fp16 norm (zeros past nb).
 template <int BITS>
-__global__ __launch_bounds__(256) void decode_kernel(const uint8_t *__restrict__ codes,
-                                                     const uint16_t *__restrict__ norms,
-                                                     uint32_t nblocks, uint32_t row_blocks,
-                                                     int64_t cache_row_blocks, int64_t t0_blocks,
-                                                     uint8_t *__restrict__ x, Codebook cb)
+__device__ __forceinline__ void load_codes(uint32_t (&W)[4 * BITS], uint16_t &N,
+                                           const uint8_t *__restrict__ codes,
+                                           const uint16_t *__restrict__ norms, uint32_t b,
+                                           uint32_t nblocks, uint32_t row_blocks,
+                                           int64_t cache_row_blocks, int64_t t0_blocks)
+{
+    if (b < nblocks) {
+        const int64_t src = cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
+        const u4_t *in = (const u4_t *)(codes + src * (16 * BITS));
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) {
+            const u4_t c = in[k];
+            W[4 * k] = c.x;
+            W[4 * k + 1] = c.y;
+            W[4 * k + 2] = c.z;
+            W[4 * k + 3] = c.w;
+        }
+        N = norms[src];
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4 * BITS; ++k)
+            W[k] = 0u;
+        N = 0;
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ norms,
+                                                        uint32_t nblocks, uint32_t row_blocks,
+                                                        int64_t cache_row_blocks,
+                                                        int64_t t0_blocks,
+                                                        uint8_t *__restrict__ x, Codebook cb)
 {
     // turbo3: 64 entries (6 code bits = two codes) -> stage-one outputs (y0+y1, y0-y1)
     // turbo2: 256 entries (8 code bits = four codes) -> stage-two outputs
@@ -272,86 +399,93 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint8_t *__restrict__
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t b0 = (blockIdx.x * kWavesPerGroup + wave) * kBlocksPerWave;
-    if (b0 >= nblocks)
+    const uint32_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
+    const uint32_t stride = gridDim.x * kWavesPerGroup;
+    uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
+    if (tile >= ntiles)
         return;
-    uint8_t *tile = smem + kTableBytes + wave * kTileBytes;
-    const uint32_t nb = min(nblocks - b0, (uint32_t)kBlocksPerWave);
-    const uint32_t b = b0 + lane;
-    const bool valid = b < nblocks;
-
+    uint8_t *lds = smem + kTableBytes + wave * kTileBytes;
     constexpr int NW = 4 * BITS;
-    uint32_t w[NW];
-    float scale = 0.0f;
-    if (valid) {
-        const int64_t src = cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
-        const u4_t *in = (const u4_t *)(codes + src * (16 * BITS));
-#pragma unroll
-        for (int k = 0; k < BITS; ++k) {
-            u4_t c = in[k];
-            w[4 * k] = c.x;
-            w[4 * k + 1] = c.y;
-            w[4 * k + 2] = c.z;
-            w[4 * k + 3] = c.w;
-        }
-        scale = (float)__builtin_bit_cast(_Float16, norms[src]) * (1.0f / 128.0f);
-    } else {
+
+    uint32_t W[NW];
+    uint16_t N;
+    load_codes<BITS>(W, N, codes, norms, tile * kBlocksPerWave + lane, nblocks, row_blocks,
+                     cache_row_blocks, t0_blocks);
+    for (;;) {
+        const uint32_t b0 = tile * kBlocksPerWave;
+        const uint32_t nb = min(nblocks - b0, (uint32_t)kBlocksPerWave);
+        uint32_t w[NW];
 #pragma unroll
         for (int k = 0; k < NW; ++k)
-            w[k] = 0u;
-    }
+            w[k] = W[k];
+        const float scale = (float)__builtin_bit_cast(_Float16, N) * (1.0f / 128.0f);
+        const uint32_t next = tile + stride;
+        if (next < ntiles)
+            load_codes<BITS>(W, N, codes, norms, next * kBlocksPerWave + lane, nblocks,
+                             row_blocks, cache_row_blocks, t0_blocks);
 
-    float u[kBlock];
-    if constexpr (BITS == 3) {
+        float u[kBlock];
+        if constexpr (BITS == 3) {
 #pragma unroll
-        for (int p = 0; p < 64; ++p) {
-            const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
-            uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
-                                  : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-            float2 t = *(const float2 *)(table + 2 * e);
-            u[2 * p] = t.x;
-            u[2 * p + 1] = t.y;
+            for (int p = 0; p < 64; ++p) {
+                const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
+                uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
+                                      : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
+                float2 t = *(const float2 *)(table + 2 * e);
+                u[2 * p] = t.x;
+                u[2 * p + 1] = t.y;
+            }
+            fwht_from<2, 64>(u);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 32; ++p) {
+                uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
+                float4 t = *(const float4 *)(table + 4 * e);
+                u[4 * p] = t.x;
+                u[4 * p + 1] = t.y;
+                u[4 * p + 2] = t.z;
+                u[4 * p + 3] = t.w;
+            }
+            fwht_from<4, 64>(u);
         }
-        fwht_from<2, 64>(u);
-    } else {
+        // last stage with the rescale by n16/128 folded in: (a +- b) s = a s +- b s
 #pragma unroll
-        for (int p = 0; p < 32; ++p) {
-            uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
-            float4 t = *(const float4 *)(table + 4 * e);
-            u[4 * p] = t.x;
-            u[4 * p + 1] = t.y;
-            u[4 * p + 2] = t.z;
-            u[4 * p + 3] = t.w;
+        for (int j = 0; j < 64; ++j) {
+            const float as = u[j] * scale, bj = u[j + 64];
+            u[j] = __builtin_fmaf(bj, scale, as);
+            u[j + 64] = __builtin_fmaf(-bj, scale, as);
         }
-        fwht_from<4, 64>(u);
-    }
-    // last stage with the rescale by n16/128 folded in: (a +- b) s = a s +- b s
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const float as = u[j] * scale, bj = u[j + 64];
-        u[j] = __builtin_fmaf(bj, scale, as);
-        u[j + 64] = __builtin_fmaf(-bj, scale, as);
-    }
 
-    // round to fp16 (nearest even) and transpose back through LDS
+        // round to fp16 (nearest even), transpose through LDS, 1 KB contiguous stores
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        uint32_t o[4];
+        for (int c = 0; c < 16; ++c) {
+            uint32_t o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            h2_t hv = {(_Float16)u[8 * c + 2 * k], (_Float16)u[8 * c + 2 * k + 1]};
-            o[k] = __builtin_bit_cast(uint32_t, hv);
+            for (int k = 0; k < 4; ++k) {
+                h2_t hv = {(_Float16)u[8 * c + 2 * k], (_Float16)u[8 * c + 2 * k + 1]};
+                o[k] = __builtin_bit_cast(uint32_t, hv);
+            }
+            *(u4_t *)(lds + swz(lane, c)) = u4_t{o[0], o[1], o[2], o[3]};
         }
-        *(u4_t *)(tile + swz(lane, c)) = u4_t{o[0], o[1], o[2], o[3]};
-    }
-    wave_lds_sync();
-    uint8_t *dst = x + (size_t)b0 * (kBlock * 2);
+        wave_lds_sync();
+        uint8_t *dst = x + (size_t)b0 * (kBlock * 2) + lane * 16;
+        if (nb == kBlocksPerWave) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        uint32_t blk = 4 * k + (lane >> 4);
-        u4_t r = *(const u4_t *)(tile + swz(blk, lane & 15u));
-        if (blk < nb)
-            *(u4_t *)(dst + k * 1024 + lane * 16) = r;
+            for (int k = 0; k < 16; ++k)
+                *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t blk = 4 * k + (lane >> 4);
+                const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
+                if (blk < nb)
+                    *(u4_t *)(dst + k * 1024) = r;
+            }
+        }
+        tile = next;
+        if (tile >= ntiles)
+            break;
+        wave_lds_sync();
     }
 }
 
@@ -499,10 +633,42 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
     }
 }
 
-inline int grid_for(int64_t nblocks)
+// Compute units of the current device (cached per device).
+int cu_count()
 {
-    int64_t per_group = (int64_t)kWavesPerGroup * kBlocksPerWave;
-    return (int)((nblocks + per_group - 1) / per_group);
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Workgroups per compute unit of a persistent grid: the kernel's own occupancy
+// (encode: three 4-wave groups, at most 168 VGPRs per lane and 3 x 32 KB of LDS;
+// decode: two groups, 2 x 64 KB of LDS and at most 256 VGPRs per lane),
+// overridable for tuning sweeps with
+// TQ_ENCODE_GROUPS_PER_CU / TQ_DECODE_GROUPS_PER_CU.
+int groups_per_cu(const char *env, int dflt)
+{
+    const char *e = getenv(env);
+    int v = e ? atoi(e) : 0;
+    return v > 0 && v <= 64 ? v : dflt;
+}
+
+// Persistent grid: at most `per_cu` groups per CU, never more groups than it takes
+// to give every wave one tile.
+inline int grid_for(int64_t nblocks, int tile_blocks, int per_cu)
+{
+    const int64_t per_group = (int64_t)kWavesPerGroup * tile_blocks;
+    const int64_t need = (nblocks + per_group - 1) / per_group;
+    const int64_t cap = (int64_t)cu_count() * per_cu;
+    return (int)(need < cap ? need : cap);
 }
 
 }  // namespace
@@ -513,7 +679,8 @@ int launch_encode(int bits, const void *x, int64_t nblocks, int64_t row_blocks,
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
-    dim3 grid(grid_for(nblocks)), block(256);
+    static const int per_cu = groups_per_cu("TQ_ENCODE_GROUPS_PER_CU", 3);
+    dim3 grid(grid_for(nblocks, kEncTileBlocks, per_cu)), block(256);
     if (bits == 3)
         hipLaunchKernelGGL(encode_kernel<3>, grid, block, 0, s, (const uint8_t *)x,
                            (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
@@ -531,7 +698,8 @@ int launch_decode(int bits, const void *codes, const void *norms, int64_t nblock
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
-    dim3 grid(grid_for(nblocks)), block(256);
+    static const int per_cu = groups_per_cu("TQ_DECODE_GROUPS_PER_CU", 2);
+    dim3 grid(grid_for(nblocks, kBlocksPerWave, per_cu)), block(256);
     if (bits == 3)
         hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, s, (const uint8_t *)codes,
                            (const uint16_t *)norms, (uint32_t)nblocks, (uint32_t)row_blocks,
