@@ -153,6 +153,53 @@ __device__ __forceinline__ void swap32(float &a, float &b)
     b = __builtin_bit_cast(float, r1);
 }
 
+// Writes a finished tile: packed codes staged in LDS (block b at b * 16 * BITS)
+// and each lane's norm.  Consecutive cache blocks (always, unless the tile
+// straddles two (layer, head) rows of a cache longer than x) leave as contiguous
+// 16-byte stores; otherwise every lane writes its two 32-code groups itself.
+template <int BITS>
+__device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t lane, uint32_t b0,
+                                               uint32_t nb, uint16_t n16, uint32_t row_blocks,
+                                               int64_t cache_row_blocks, int64_t t0_blocks,
+                                               uint8_t *__restrict__ codes,
+                                               uint16_t *__restrict__ norms)
+{
+    constexpr int GW = BITS, GB = 4 * BITS, CB = 16 * BITS;
+    const uint32_t blk = lane & 31u, half = lane >> 5;
+    const int64_t dst0 = cache_block(b0, row_blocks, cache_row_blocks, t0_blocks);
+    const int64_t dstl = cache_block(b0 + nb - 1, row_blocks, cache_row_blocks, t0_blocks);
+    if (dstl - dst0 == (int64_t)nb - 1) {
+        uint8_t *gdst = codes + dst0 * CB;
+        const uint32_t nchunks = nb * BITS;   // 16-byte chunks of the tile's codes
+#pragma unroll
+        for (int k = 0; k < (2 * BITS + 3) / 4; ++k) {
+            const uint32_t c = k * 64 + lane;
+            if (c < 2u * BITS * 16u) {
+                const u4_t val = *(const u4_t *)(stage + c * 16);
+                if (c < nchunks)
+                    *(u4_t *)(gdst + c * 16) = val;
+            }
+        }
+        if (blk < nb && half == 0)
+            norms[dst0 + blk] = n16;
+    } else if (blk < nb) {
+        const int64_t dst = cache_block(b0 + blk, row_blocks, cache_row_blocks, t0_blocks);
+        const uint32_t *src = (const uint32_t *)(stage + blk * CB + GB * half);
+        uint32_t *out = (uint32_t *)(codes + dst * CB + GB * half);
+#pragma unroll
+        for (int k = 0; k < GW; ++k) {
+            out[k] = src[k];
+            out[2 * GW + k] = src[2 * GW + k];
+        }
+        if (half == 0)
+            norms[dst] = n16;
+    }
+}
+
+// Per iteration (tile i): park tile i in LDS, write out tile i-1 (finished in the
+// previous iteration), issue the loads of tile i+1, then compute tile i.  The
+// stores and the next loads are both issued before the compute, so neither the
+// load latency nor the store completions hold the wave at its next wait.
 template <int BITS>
 __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restrict__ x,
                                                         uint32_t nblocks, uint32_t row_blocks,
@@ -161,31 +208,40 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
                                                         uint8_t *__restrict__ codes,
                                                         uint16_t *__restrict__ norms, Codebook cb)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile_all[kWavesPerGroup][kEncTileBytes];
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    constexpr int GW = BITS;              // 32-bit words per 32-code group
+    constexpr int GB = 4 * BITS;          // bytes per 32-code group
+    constexpr int CB = 16 * BITS;         // code bytes per block
+    constexpr int kStage = kEncTileBlocks * 48;
+    constexpr float mid = (float)(1 << (BITS - 1));
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWavesPerGroup][kEncTileBytes + kStage];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
     const uint32_t blk = lane & 31u, half = lane >> 5;
     const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
     const uint32_t stride = gridDim.x * kWavesPerGroup;
     uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
     if (tile >= ntiles)
         return;
-    uint8_t *lds = tile_all[wave];
-    constexpr int GW = BITS;              // 32-bit words per 32-code group
-    constexpr int GB = 4 * BITS;          // bytes per 32-code group
-    constexpr int CB = 16 * BITS;         // code bytes per block
-    constexpr float mid = (float)(1 << (BITS - 1));
+    uint8_t *lds = lds_all[wave];
+    uint8_t *stage = lds + kEncTileBytes;
 
     u4_t R[8];
     load_enc_tile(R, x, tile * kEncTileBlocks, min(nblocks - tile * kEncTileBlocks, 32u), lane);
+    uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in `stage`
+    uint16_t pn16 = 0;
     for (;;) {
         const uint32_t b0 = tile * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
 
-        // 1. park the tile in LDS (XOR-swizzled), then prefetch the next one into R
+        // 1. park the tile in LDS (XOR-swizzled); write out the previous tile; then
+        //    start loading the next one into R
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             *(u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)) = R[k];
         wave_lds_sync();
+        if (pnb)
+            store_enc_tile<BITS>(stage, lane, pb0, pnb, pn16, row_blocks, cache_row_blocks,
+                                 t0_blocks, codes, norms);
         const uint32_t next = tile + stride;
         if (next < ntiles)
             load_enc_tile(R, x, next * kEncTileBlocks,
@@ -201,7 +257,6 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
             v[4 * c + 2] = as_h2(wv.z);
             v[4 * c + 3] = as_h2(wv.w);
         }
-        wave_lds_sync();   // the tile area is reused below for the packed codes
 
         // 3. rotation, with the norm's sum of squares (exact fp16 squares, four
         //    partial sums) taken from the same pairs.  Spans 1 and 2 come straight
@@ -254,7 +309,7 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
             u[i + 32] = a - b;
         }
 
-        // 5. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F); the
+        // 4. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F); the
         //    coefficients absorb 1/n and the clamp is scaled by n, so no division per
         //    value; g is odd, so a negated u[r] negates the last product.  n == 0
         //    (zero block) gives F = 2^b/2 for every value.
@@ -285,52 +340,28 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
             if (sh + BITS > 32)
                 w[wi + 1] |= code >> (32 - sh);
         }
-        const uint16_t n16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf(n, 65504.0f));
 
-        // 6. store.  Consecutive cache blocks (always, unless the tile straddles two
-        //    (layer, head) rows of a cache longer than x): stage the tile's codes in
-        //    LDS and write them as contiguous 16-byte stores.
-        const int64_t dst0 = cache_block(b0, row_blocks, cache_row_blocks, t0_blocks);
-        const int64_t dstl = cache_block(b0 + nb - 1, row_blocks, cache_row_blocks, t0_blocks);
-        const bool live = blk < nb;
-        if (dstl - dst0 == (int64_t)nb - 1) {
-            uint32_t *st = (uint32_t *)(lds + blk * CB + GB * half);
+        // 5. stage the packed groups at their place in the block (low lane: code bytes
+        //    [0, GB) and [2 GB, 3 GB); high lane: [GB, 2 GB) and [3 GB, 4 GB)); they
+        //    leave at the start of the next iteration (or after the loop)
+        {
+            uint32_t *st = (uint32_t *)(stage + blk * CB + GB * half);
 #pragma unroll
             for (int k = 0; k < GW; ++k) {
                 st[k] = wa[k];
                 st[2 * GW + k] = wb[k];
             }
-            wave_lds_sync();
-            uint8_t *gdst = codes + dst0 * CB;
-            const uint32_t nchunks = nb * BITS;   // 16-byte chunks of the tile's codes
-#pragma unroll
-            for (int k = 0; k < (2 * BITS + 3) / 4; ++k) {
-                const uint32_t c = k * 64 + lane;
-                if (c < 2u * BITS * 16u) {
-                    const u4_t val = *(const u4_t *)(lds + c * 16);
-                    if (c < nchunks)
-                        *(u4_t *)(gdst + c * 16) = val;
-                }
-            }
-            if (live && half == 0)
-                norms[dst0 + blk] = n16;
-        } else if (live) {
-            const int64_t dst = cache_block(b0 + blk, row_blocks, cache_row_blocks, t0_blocks);
-            uint32_t *out = (uint32_t *)(codes + dst * CB + GB * half);
-#pragma unroll
-            for (int k = 0; k < GW; ++k) {
-                out[k] = wa[k];
-                out[2 * GW + k] = wb[k];
-            }
-            if (half == 0)
-                norms[dst] = n16;
         }
-
+        pb0 = b0;
+        pnb = nb;
+        pn16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf(n, 65504.0f));
+        wave_lds_sync();   // staged codes visible; this tile's LDS reads are done
         tile = next;
         if (tile >= ntiles)
             break;
-        wave_lds_sync();   // the staged codes are read before the next tile lands
     }
+    store_enc_tile<BITS>(stage, lane, pb0, pnb, pn16, row_blocks, cache_row_blocks, t0_blocks,
+                         codes, norms);
 }
 
 // ---------------------------------------------------------------- decode
@@ -360,6 +391,26 @@ __device__ __forceinline__ void load_codes(uint32_t (&W)[4 * BITS], uint16_t &N,
         for (int k = 0; k < 4 * BITS; ++k)
             W[k] = 0u;
         N = 0;
+    }
+}
+
+// Writes a decoded tile from its LDS image: 1 KB contiguous 16-byte stores.
+__device__ __forceinline__ void store_dec_tile(const uint8_t *lds, uint32_t lane, uint32_t b0,
+                                               uint32_t nb, uint8_t *__restrict__ x)
+{
+    uint8_t *dst = x + (size_t)b0 * (kBlock * 2) + lane * 16;
+    if (nb == kBlocksPerWave) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t blk = 4 * k + (lane >> 4);
+            const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
+            if (blk < nb)
+                *(u4_t *)(dst + k * 1024) = r;
+        }
     }
 }
 
@@ -398,7 +449,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
     }
     __syncthreads();
 
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
     const uint32_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
     const uint32_t stride = gridDim.x * kWavesPerGroup;
     uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
@@ -407,10 +459,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
     uint8_t *lds = smem + kTableBytes + wave * kTileBytes;
     constexpr int NW = 4 * BITS;
 
+    // Per iteration (tile i): take tile i's codes (prefetched), write out tile i-1
+    // from LDS, issue the loads of tile i+1, then compute tile i into LDS.  Stores
+    // and loads are both issued before the compute, so the wave's next wait finds
+    // them complete.
     uint32_t W[NW];
     uint16_t N;
     load_codes<BITS>(W, N, codes, norms, tile * kBlocksPerWave + lane, nblocks, row_blocks,
                      cache_row_blocks, t0_blocks);
+    uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in LDS
     for (;;) {
         const uint32_t b0 = tile * kBlocksPerWave;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kBlocksPerWave);
@@ -419,6 +476,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
         for (int k = 0; k < NW; ++k)
             w[k] = W[k];
         const float scale = (float)__builtin_bit_cast(_Float16, N) * (1.0f / 128.0f);
+        if (pnb)
+            store_dec_tile(lds, lane, pb0, pnb, x);
         const uint32_t next = tile + stride;
         if (next < ntiles)
             load_codes<BITS>(W, N, codes, norms, next * kBlocksPerWave + lane, nblocks,
@@ -456,7 +515,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
             u[j + 64] = __builtin_fmaf(-bj, scale, as);
         }
 
-        // round to fp16 (nearest even), transpose through LDS, 1 KB contiguous stores
+        // round to fp16 (nearest even) into the LDS tile (block per lane, swizzled)
+        wave_lds_sync();   // the previous tile's rows have been read out
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             uint32_t o[4];
@@ -468,25 +528,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
             *(u4_t *)(lds + swz(lane, c)) = u4_t{o[0], o[1], o[2], o[3]};
         }
         wave_lds_sync();
-        uint8_t *dst = x + (size_t)b0 * (kBlock * 2) + lane * 16;
-        if (nb == kBlocksPerWave) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
-        } else {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t blk = 4 * k + (lane >> 4);
-                const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
-                if (blk < nb)
-                    *(u4_t *)(dst + k * 1024) = r;
-            }
-        }
+        pb0 = b0;
+        pnb = nb;
         tile = next;
         if (tile >= ntiles)
             break;
-        wave_lds_sync();
     }
+    store_dec_tile(lds, lane, pb0, pnb, x);
 }
 
 // ---------------------------------------------------------------- q.K scores
@@ -549,7 +597,8 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
         __syncthreads();
     }
 
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
     const uint32_t lpt = 1u << lpt_log2, tpw = 64u >> lpt_log2;
     const uint32_t tok = lane >> lpt_log2, sub = lane & (lpt - 1u);
     const uint32_t slice = sub >> 2, part = sub & 3u;
