@@ -6,12 +6,13 @@ Workload: one layer of a GQA model's cache, K and V fp16 [8 kv heads, 32768
 tokens, 128], N(0,1) with 3 of 128 channels (2%) scaled x20 and a per-token
 scale log-uniform on [0.5, 4] (synthetic, seeded; generated on the GPU).
 
-One step runs the whole path once:
-  turbo3 encode K, V   turbo2 encode K, V   turbo3 decode K, V   turbo2 decode K, V
+K and V are held as one [2, 8, 32768, 128] tensor, so each op below is one launch
+covering both.  One step runs the whole path once:
+  turbo3 encode of K,V   turbo2 encode of K,V   turbo3 decode   turbo2 decode
   1-token append of K and V (turbo3, row 32767)
   fused q.K scores of 32 query heads (GQA group 4) against the turbo3 K cache.
-Each type encodes its own copy of K and V and decodes into its own buffers, so
-no op re-reads data another op of the step left in the 256 MB Infinity Cache.
+Each type encodes its own copy of K,V and decodes into its own buffers, so no
+op re-reads data another op of the step left in the 256 MB Infinity Cache.
 
 Printed: one JSON line.  value = algorithmic bytes of the step / wall time per
 step (GB/s); the dominant kernel's roofline is timed with HIP events on the
@@ -35,7 +36,7 @@ METRIC = "turbo3/turbo2 KV encode+decode GB/s and fraction of HBM peak, 1 MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 L, H, T, D = 1, 8, 32768, 128  # one layer
 HQ = 32                        # query heads (GQA group 4)
-SEED = 2
+COPY_CAL_BYTES = 256 << 20     # bytes read (and written) by one calibration copy
 
 
 def codec_bytes(nblocks: int, bits: int) -> int:
@@ -55,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (default: usable cores, at most 16)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run three plain 256 MiB device copies (a kernel "
+                         "of known traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -79,91 +83,104 @@ def main():
 
     w = gen.WORKLOADS["one_layer"]
     m = D // 128
-    K = torch.empty((L, H, T, D), dtype=torch.float16, device=dev)
-    V = torch.empty_like(K)
-    K[0] = gen.kv_layer(w.seed, "K", w.spec, 0, H, T, D, device=dev)
-    V[0] = gen.kv_layer(w.seed, "V", w.spec, 0, H, T, D, device=dev)
+    # K and V of the layer as one [2, H, T, D] tensor (index 0 = K, 1 = V): every op
+    # of the step handles both in a single launch.
+    KV = torch.empty((2, H, T, D), dtype=torch.float16, device=dev)
+    KV[0] = gen.kv_layer(w.seed, "K", w.spec, 0, H, T, D, device=dev)
+    KV[1] = gen.kv_layer(w.seed, "V", w.spec, 0, H, T, D, device=dev)
     q = gen.queries(w.seed, 1, HQ, D, device=dev)
-    tok_k = gen.kv_layer(w.seed + 100, "K", w.spec, 0, H, 1, D, device=dev).unsqueeze(0)
-    tok_v = gen.kv_layer(w.seed + 100, "V", w.spec, 0, H, 1, D, device=dev).unsqueeze(0)
+    tok = torch.empty((2, H, 1, D), dtype=torch.float16, device=dev)
+    tok[0] = gen.kv_layer(w.seed + 100, "K", w.spec, 0, H, 1, D, device=dev)
+    tok[1] = gen.kv_layer(w.seed + 100, "V", w.spec, 0, H, 1, D, device=dev)
 
     bufs = {}
     for bits in (3, 2):
-        bufs[bits] = dict(
-            K=K.clone(), V=V.clone(),
-            cK=tq.empty_cache(bits, L, H, T, D, dev), cV=tq.empty_cache(bits, L, H, T, D, dev),
-            oK=torch.empty_like(K), oV=torch.empty_like(K))
+        bufs[bits] = dict(x=KV.clone(), c=tq.empty_cache(bits, 2, H, T, D, dev),
+                          o=torch.empty_like(KV))
     scores = torch.empty((1, HQ, T), dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(D)
-    nblk = L * H * T * m
+    nblk = 2 * H * T * m          # K and V blocks
 
     ops = []   # (name, bytes, fn)
     for bits in (3, 2):
         b = bufs[bits]
-        ops.append((f"encode_turbo{bits}_K", codec_bytes(nblk, bits),
-                    lambda b=b, bits=bits: tq.tq_encode(bits, b["K"], *b["cK"], 0)))
-        ops.append((f"encode_turbo{bits}_V", codec_bytes(nblk, bits),
-                    lambda b=b, bits=bits: tq.tq_encode(bits, b["V"], *b["cV"], 0)))
+        ops.append((f"encode_turbo{bits}", codec_bytes(nblk, bits),
+                    lambda b=b, bits=bits: tq.tq_encode(bits, b["x"], *b["c"], 0)))
     for bits in (3, 2):
         b = bufs[bits]
-        ops.append((f"decode_turbo{bits}_K", codec_bytes(nblk, bits),
-                    lambda b=b, bits=bits: tq.tq_decode(bits, *b["cK"], 0, b["oK"])))
-        ops.append((f"decode_turbo{bits}_V", codec_bytes(nblk, bits),
-                    lambda b=b, bits=bits: tq.tq_decode(bits, *b["cV"], 0, b["oV"])))
-    b3 = bufs[3]
-    ops.append(("append_turbo3_K", codec_bytes(L * H * m, 3),
-                lambda: tq.tq_encode(3, tok_k, *b3["cK"], T - 1)))
-    ops.append(("append_turbo3_V", codec_bytes(L * H * m, 3),
-                lambda: tq.tq_encode(3, tok_v, *b3["cV"], T - 1)))
-    ops.append(("qk_turbo3", qk_bytes(L, H, T, m, HQ, 3),
-                lambda: tq.tq_qk_scores(3, *b3["cK"], q, scale, scores)))
+        ops.append((f"decode_turbo{bits}", codec_bytes(nblk, bits),
+                    lambda b=b, bits=bits: tq.tq_decode(bits, *b["c"], 0, b["o"])))
+    c3, n3 = bufs[3]["c"]
+    kc, kn = c3[0:1], n3[0:1]     # the K half of the turbo3 cache, [1, H, T, D/128, 48]
+    ops.append(("append_turbo3", codec_bytes(2 * H * m, 3),
+                lambda: tq.tq_encode(3, tok, c3, n3, T - 1)))
+    ops.append(("qk_turbo3", qk_bytes(1, H, T, m, HQ, 3),
+                lambda: tq.tq_qk_scores(3, kc, kn, q, scale, scores)))
     step_bytes = sum(o[1] for o in ops)
 
-    def step(events=None):
+    def step(dom_i=-1, ev=None):
         for i, (_, _, fn) in enumerate(ops):
-            if events is not None:
-                events[i][0].record(stream)
+            if i == dom_i:
+                ev[0].record(stream)
             fn()
-            if events is not None:
-                events[i][1].record(stream)
+            if i == dom_i:
+                ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, wall clock between two device synchronisations
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(args.steps)]
+    # per-op durations: each op launched back to back REPS times between two events
+    reps = 20
+    per_op = {}
+    for name, nbytes, fn in ops:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        per_op[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    dom = max(per_op, key=lambda k: per_op[k]["us"])   # the dominant kernel of the step
+    dom_i = [o[0] for o in ops].index(dom)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, wall clock between two device synchronisations; the
+    # dominant kernel's launches are bracketed by HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
+    for s_ in range(args.steps):
+        step(dom_i, ev[s_])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes * args.steps / elapsed / 1e9
 
-    per_op = {}
-    for i, (name, nbytes, _) in enumerate(ops):
-        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-        per_op[name] = {"us": round(ms * 1e3, 2), "bytes": nbytes,
-                        "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-    # dominant kernel = the op family with the largest share of the step
-    fam = {}
-    for name, rec in per_op.items():
-        key = name.rsplit("_", 1)[0] if name.endswith(("_K", "_V")) else name
-        fam.setdefault(key, []).append(rec)
-    dom = max(fam, key=lambda k: sum(r["us"] for r in fam[k]))
-    d_us = sum(r["us"] for r in fam[dom]) / len(fam[dom])
-    d_bytes = fam[dom][0]["bytes"]
+    d_bytes = per_op[dom]["bytes"]
+    d_us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / args.steps
     achieved = d_bytes / (d_us * 1e-6) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "bytes_per_launch": d_bytes, "avg_launch_us": round(d_us, 2)}
+                "traffic": measured_traffic(dom), "bytes_per_launch": d_bytes,
+                "avg_launch_us": round(d_us, 2)}
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(K, V, q, tok_k, tok_v, scale, step_bytes, args.cpu_threads)
+        cpu = cpu_baseline(KV, q, tok, scale, step_bytes, args.cpu_threads)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -173,7 +190,7 @@ def main():
         "config": {"workload": "one_layer: K,V fp16 [8 kv_heads, 32768 tokens, 128]; turbo3+turbo2 "
                                "encode+decode of K and V, 1-token turbo3 append, turbo3 q.K of 32 "
                                "query heads (GQA 4)",
-                   "bytes_per_step": step_bytes, "values_per_step_codec": 8 * nblk * 128,
+                   "bytes_per_step": step_bytes, "values_per_step_codec": 4 * nblk * 128,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -182,31 +199,55 @@ def main():
     print(json.dumps(out))
 
 
-def cpu_baseline(K, V, q, tok_k, tok_v, scale, step_bytes, threads):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_turbo3_one_layer_kv_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_quantization_block_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or None when no
+    summary covers this kernel or the kernel source changed since it was taken."""
+    import hashlib
+    if kernel != "encode_turbo3" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.split("#")[0].strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != sha:
+        return None
+    copy_kib = int(rec["copy_bytes"]) / 1024
+    fetch = float(rec["fetch_size_kib"]) * copy_kib / float(rec["copy_fetch_size_kib"])
+    write = float(rec["write_size_kib"]) * copy_kib / float(rec["copy_write_size_kib"])
+    return int(round((fetch + write) * 1024))
+
+
+def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
     """The CPU oracle, untuned, on one full step of the same inputs (host copies)."""
     import numpy as np
 
     import oracle
     if threads <= 0:
         threads = min(len(os.sched_getaffinity(0)), 16)
-    Kn, Vn = K.cpu().numpy(), V.cpu().numpy()
+    x = KV.cpu().numpy()
     qn = q.cpu().numpy()
-    tk, tv = tok_k.cpu().numpy(), tok_v.cpu().numpy()
+    tk = tok.cpu().numpy()
     m = D // 128
     t0 = time.perf_counter()
     caches = {}
     for bits in (3, 2):
-        for name, x in (("K", Kn), ("V", Vn)):
-            c = np.zeros((L, H, T, m, 16 * bits), np.uint8)
-            n = np.zeros((L, H, T, m), np.float16)
-            oracle.encode(bits, x, c, n, nthreads=threads)
-            caches[(bits, name)] = (c, n)
+        c = np.zeros((2, H, T, m, 16 * bits), np.uint8)
+        n = np.zeros((2, H, T, m), np.float16)
+        oracle.encode(bits, x, c, n, nthreads=threads)
+        caches[bits] = (c, n)
     for bits in (3, 2):
-        for name in ("K", "V"):
-            oracle.decode(bits, *caches[(bits, name)], 0, T, nthreads=threads)
-    oracle.encode(3, tk, *caches[(3, "K")], t0=T - 1, nthreads=threads)
-    oracle.encode(3, tv, *caches[(3, "V")], t0=T - 1, nthreads=threads)
-    oracle.qk_scores(3, *caches[(3, "K")], qn, scale, nthreads=threads)
+        oracle.decode(bits, *caches[bits], 0, T, nthreads=threads)
+    oracle.encode(3, tk, *caches[3], t0=T - 1, nthreads=threads)
+    c3, n3 = caches[3]
+    oracle.qk_scores(3, c3[0:1], n3[0:1], qn, scale, nthreads=threads)
     el = time.perf_counter() - t0
     return {"value": round(step_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(el, 2),

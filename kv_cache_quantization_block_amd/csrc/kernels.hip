@@ -74,6 +74,14 @@ __device__ __forceinline__ float dot2(h2_t a, h2_t b)
     return d;
 }
 
+// The value of another lane of the same quad (DPP quad_perm pattern CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
 // Order LDS traffic between the lanes of one wavefront (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -539,24 +547,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
 
 // ---------------------------------------------------------------- q.K scores
 
-constexpr int kQkTokensPerGroup = 1024;
+// Token groups per wave whose codes are in flight while the previous groups are
+// scored (a group is the tokens one wave scores at once).
+constexpr int kQkDepth = 4;
 
 // BITS: 2 or 3.  GH: query heads per pass (1, 2 or 4).  LPT: lanes per key token
 // (4 * next power of two of m); lane = token * LPT + slice * 4 + part, the lane
-// covers values [32*part, 32*part + 32) of 128-block `slice` of the token.
+// covers values [32*part, 32*part + 32) of 128-block `slice` of the token.  A
+// workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head)
+// for GH query heads.
 template <int BITS, int GH>
-__global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_codes,
-                                                 const uint16_t *__restrict__ k_norms,
-                                                 const uint16_t *__restrict__ q,
-                                                 float *__restrict__ scores, uint32_t Hkv,
-                                                 int64_t Tc, uint32_t T, uint32_t m,
-                                                 uint32_t lpt_log2, uint32_t G, uint32_t Hq,
-                                                 uint32_t passes, float scale, Codebook cb)
+__global__ __launch_bounds__(256, 2) void qk_kernel(const uint8_t *__restrict__ k_codes,
+                                                    const uint16_t *__restrict__ k_norms,
+                                                    const uint16_t *__restrict__ q,
+                                                    float *__restrict__ scores, uint32_t Hkv,
+                                                    int64_t Tc, uint32_t T, uint32_t m,
+                                                    uint32_t lpt_log2, uint32_t G, uint32_t Hq,
+                                                    uint32_t passes, uint32_t tpg, float scale,
+                                                    Codebook cb)
 {
-    // turbo3: 64 entries (two codes) -> (y0, y1); turbo2: 256 entries (four codes) -> y0..y3
+    // turbo3: 64 entries (two codes) -> (y0, y1); turbo2: 256 entries (four codes) ->
+    // y0..y3.  NC copies of the table interleaved entry by entry: copy c of entry e
+    // sits at (e * NC + c) * EW floats, and lane l reads copy l % NC, so the lanes
+    // one LDS cycle serves (16 lanes x 8 B, 8 lanes x 16 B) hit distinct banks
+    // whatever codes they look up.
     constexpr int NE = BITS == 3 ? 64 : 256;
     constexpr int EW = BITS == 3 ? 2 : 4;
-    constexpr int kTableFloats = NE * EW;
+    constexpr int NC = BITS == 3 ? 16 : 8;
+    constexpr int kTableFloats = NE * EW * NC;
     // one LDS buffer, the lookup table first (addressed by code bits alone), then
     // the rotated query slices qs[head * m + slice][i]
     __shared__ __attribute__((aligned(16))) float smem[kTableFloats + GH * 16 * kBlock];
@@ -568,14 +586,15 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
     const uint32_t b = bg / Hkv, g = bg - b * Hkv;
     const uint32_t h0 = g * G + pass * GH;             // first query head of this pass
 
-    for (int e = threadIdx.x; e < NE; e += blockDim.x) {
+    for (int i = threadIdx.x; i < NE * NC; i += blockDim.x) {
+        const int e = i / NC;   // entry i / NC, copy i % NC
         if constexpr (BITS == 3) {
-            table[2 * e] = cb.levels[e & 7];
-            table[2 * e + 1] = cb.levels[e >> 3];
+            table[2 * i] = cb.levels[e & 7];
+            table[2 * i + 1] = cb.levels[e >> 3];
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                table[4 * e + k] = cb.levels[(e >> (2 * k)) & 3];
+                table[4 * i + k] = cb.levels[(e >> (2 * k)) & 3];
         }
     }
     // load the GH x m query slices as float, then rotate each in place
@@ -603,6 +622,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
     const uint32_t tok = lane >> lpt_log2, sub = lane & (lpt - 1u);
     const uint32_t slice = sub >> 2, part = sub & 3u;
     const bool active = slice < m;
+    const float *tcopy = table + (lane % NC) * EW;   // this lane's table copy
     float qr[GH][32];
 #pragma unroll
     for (int h = 0; h < GH; ++h)
@@ -610,18 +630,16 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
         for (int i = 0; i < 32; ++i)
             qr[h][i] = active ? qs[h * m + slice][32 * part + i] : 0.0f;
 
-    const uint32_t t_begin = blockIdx.y * kQkTokensPerGroup;
-    const uint32_t t_end = min(T, t_begin + kQkTokensPerGroup);
+    const uint32_t t_begin = blockIdx.y * tpg;
+    const uint32_t t_end = min(T, t_begin + tpg);
     const size_t row0 = (size_t)bg * Tc;                // first cache row of (b, g)
     constexpr int CB = 16 * BITS;                        // code bytes per block
     constexpr int LW = BITS;                             // 32-bit words per lane (32 codes)
+    const uint32_t step = kWavesPerGroup * tpw;          // tokens between a wave's groups
 
-    for (uint32_t tb = t_begin + wave * tpw; tb < t_end; tb += kWavesPerGroup * tpw) {
-        const uint32_t t = tb + tok;
-        const bool live = active && t < t_end;
-        uint32_t w[LW];
-        float f = 0.0f;
-        if (live) {
+    // the codes and norm of this lane's slice of token t (zeros when not live)
+    auto fetch = [&](uint32_t t, uint32_t (&w)[LW], float &f) {
+        if (active && t < t_end) {
             const size_t blk = (row0 + t) * m + slice;
             const uint32_t *src = (const uint32_t *)(k_codes + blk * CB + part * (4 * BITS));
 #pragma unroll
@@ -632,53 +650,89 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint8_t *__restrict__ k_c
 #pragma unroll
             for (int k = 0; k < LW; ++k)
                 w[k] = 0u;
+            f = 0.0f;
         }
-        float acc[GH];
+    };
+
+    uint32_t wn[kQkDepth][LW];
+    float fn[kQkDepth];
+    uint32_t tb = t_begin + wave * tpw;   // first token of this wave's current group
 #pragma unroll
-        for (int h = 0; h < GH; ++h)
-            acc[h] = 0.0f;
-        if constexpr (BITS == 3) {
+    for (int d = 0; d < kQkDepth; ++d)
+        fetch(tb + d * step + tok, wn[d], fn[d]);
+    while (tb < t_end) {
+        uint32_t wc[kQkDepth][LW];
+        float fc[kQkDepth];
 #pragma unroll
-            for (int p = 0; p < 16; ++p) {
-                const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
-                uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
-                                      : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-                float2 y = *(const float2 *)(table + 2 * e);
+        for (int d = 0; d < kQkDepth; ++d) {
 #pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    acc[h] = __builtin_fmaf(qr[h][2 * p], y.x, acc[h]);
-                    acc[h] = __builtin_fmaf(qr[h][2 * p + 1], y.y, acc[h]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
-                float4 y = *(const float4 *)(table + 4 * e);
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    acc[h] = __builtin_fmaf(qr[h][4 * p], y.x, acc[h]);
-                    acc[h] = __builtin_fmaf(qr[h][4 * p + 1], y.y, acc[h]);
-                    acc[h] = __builtin_fmaf(qr[h][4 * p + 2], y.z, acc[h]);
-                    acc[h] = __builtin_fmaf(qr[h][4 * p + 3], y.w, acc[h]);
-                }
-            }
+            for (int k = 0; k < LW; ++k)
+                wc[d][k] = wn[d][k];
+            fc[d] = fn[d];
         }
-        // per-slice norm, then sum the LPT lanes of the token
+        const uint32_t tn = tb + kQkDepth * step;
+        if (tn < t_end) {
 #pragma unroll
-        for (int h = 0; h < GH; ++h)
-            acc[h] *= f;
-        for (uint32_t s = 1; s < lpt; s <<= 1)
+            for (int d = 0; d < kQkDepth; ++d)
+                fetch(tn + d * step + tok, wn[d], fn[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < kQkDepth; ++d) {
+            const uint32_t t = tb + d * step + tok;
+            const uint32_t *w = wc[d];
+            float acc[GH];
 #pragma unroll
             for (int h = 0; h < GH; ++h)
-                acc[h] += __shfl_xor(acc[h], (int)s, 64);
-        if (t < t_end && sub < GH) {
-            float r = acc[0];
+                acc[h] = 0.0f;
+            if constexpr (BITS == 3) {
 #pragma unroll
-            for (int h = 1; h < GH; ++h)
-                r = sub == (uint32_t)h ? acc[h] : r;
-            scores[((size_t)b * Hq + h0 + sub) * T + t] = scale * r;
+                for (int p = 0; p < 16; ++p) {
+                    const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
+                    uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
+                                          : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
+                    float2 y = *(const float2 *)(tcopy + e * (NC * EW));
+#pragma unroll
+                    for (int h = 0; h < GH; ++h) {
+                        acc[h] = __builtin_fmaf(qr[h][2 * p], y.x, acc[h]);
+                        acc[h] = __builtin_fmaf(qr[h][2 * p + 1], y.y, acc[h]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
+                    float4 y = *(const float4 *)(tcopy + e * (NC * EW));
+#pragma unroll
+                    for (int h = 0; h < GH; ++h) {
+                        acc[h] = __builtin_fmaf(qr[h][4 * p], y.x, acc[h]);
+                        acc[h] = __builtin_fmaf(qr[h][4 * p + 1], y.y, acc[h]);
+                        acc[h] = __builtin_fmaf(qr[h][4 * p + 2], y.z, acc[h]);
+                        acc[h] = __builtin_fmaf(qr[h][4 * p + 3], y.w, acc[h]);
+                    }
+                }
+            }
+            // per-slice norm (and the score scale), then sum the LPT lanes of the token
+#pragma unroll
+            for (int h = 0; h < GH; ++h)
+                acc[h] *= fc[d] * scale;
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                acc[h] += dpp_f32<0xB1>(acc[h]);   // lane ^ 1 (quad_perm 1,0,3,2)
+                acc[h] += dpp_f32<0x4E>(acc[h]);   // lane ^ 2 (quad_perm 2,3,0,1)
+            }
+            for (uint32_t sft = 4; sft < lpt; sft <<= 1)
+#pragma unroll
+                for (int h = 0; h < GH; ++h)
+                    acc[h] += __shfl_xor(acc[h], (int)sft, 64);
+            if (t < t_end && sub < GH) {
+                float r = acc[0];
+#pragma unroll
+                for (int h = 1; h < GH; ++h)
+                    r = sub == (uint32_t)h ? acc[h] : r;
+                scores[((size_t)b * Hq + h0 + sub) * T + t] = r;
+            }
         }
+        tb = tn;
     }
 }
 
@@ -774,13 +828,26 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
         mp <<= 1;
         ++lpt_log2;
     }
-    dim3 grid((uint32_t)(B * Hkv * passes), (uint32_t)((T + kQkTokensPerGroup - 1) / kQkTokensPerGroup));
+    // Rows per workgroup: enough workgroups to fill the chip several times over,
+    // whole rounds of kQkDepth groups per wave, at most 65535 row chunks.
+    const int64_t step = (int64_t)kWavesPerGroup * (64 >> lpt_log2) * kQkDepth;
+    const int64_t pairs = B * Hkv * passes;
+    int64_t tpg = (T * pairs) / ((int64_t)cu_count() * 8);
+    tpg = tpg < (T + 65534) / 65535 ? (T + 65534) / 65535 : tpg;
+    tpg = ((tpg + step - 1) / step) * step;
+    if (tpg < step)
+        tpg = step;
+    if (tpg > 8192)
+        tpg = ((8192 + step - 1) / step) * step;
+    if ((T + tpg - 1) / tpg > 65535)
+        tpg = (((T + 65534) / 65535 + step - 1) / step) * step;
+    dim3 grid((uint32_t)pairs, (uint32_t)((T + tpg - 1) / tpg));
     dim3 block(256);
 #define TQ_QK_LAUNCH(BB, GG)                                                                    \
     hipLaunchKernelGGL((qk_kernel<BB, GG>), grid, block, 0, s, (const uint8_t *)k_codes,        \
                        (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,   \
                        Tc, (uint32_t)T, (uint32_t)m, lpt_log2, (uint32_t)G, (uint32_t)Hq,      \
-                       (uint32_t)passes, scale, *cb)
+                       (uint32_t)passes, (uint32_t)tpg, scale, *cb)
     if (bits == 3) {
         if (GH == 4) TQ_QK_LAUNCH(3, 4);
         else if (GH == 2) TQ_QK_LAUNCH(3, 2);
