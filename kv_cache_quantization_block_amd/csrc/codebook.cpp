@@ -83,7 +83,7 @@ void build(int bits, Codebook *cb)
         double tau = th[P];
         cb->g1 = (float)(1.0 / tau);
         cb->g2 = cb->g3 = 0.0f;
-        cb->clamp_t = (float)(1.9 * tau);
+        cb->clamp_t = (float)(1.9 * tau);   // F in [0.1, 3.9]
     } else {
         // three positive thresholds: g(t) = g1 t + g2 t|t| + g3 t^3 through (tau_k, k)
         double M[3][3], r[3], c[3];

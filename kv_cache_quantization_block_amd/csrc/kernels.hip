@@ -58,6 +58,16 @@ __device__ __forceinline__ uint32_t swz(uint32_t blk, uint32_t chunk)
 // this compiler, so vector elements always go through a scalar first.
 __device__ __forceinline__ h2_t as_h2(uint32_t word) { return __builtin_bit_cast(h2_t, word); }
 
+// Streaming global accesses.  Each call touches every byte of its K/V values,
+// codes, norms and scores exactly once, so all of them carry the non-temporal
+// hint: loads do not allocate in the 256 MB memory-side cache (an allocation that
+// evicts a dirty line costs a write-back inside this kernel), and stores leave no
+// dirty lines there for the next kernel to write back.
+template <class T>
+__device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void st_stream(T *p, T v) { __builtin_nontemporal_store(v, p); }
+
 // d = a.x * b.x + a.y * b.y + c in the three-operand VOP3P form (the compiler's
 // accumulate-in-place form would need a register copy per result here).
 // fp16 x (+-1) products are exact, the sum is a float.
@@ -81,6 +91,20 @@ __device__ __forceinline__ float dpp_f32(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                  0xF, 0xF, false));
 }
+
+// (a << S) + b as one v_lshl_add_u32 (kept as written: the compiler would otherwise
+// re-associate a chain of these into more instructions).
+template <int S>
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "i"(S), "v"(b));
+    return d;
+}
+
+// Float rounding mode of this wave (MODE.FP_ROUND, single-precision field).
+__device__ __forceinline__ void set_f32_round_down() { __builtin_amdgcn_s_setreg(0x801, 2); }
+__device__ __forceinline__ void set_f32_round_nearest() { __builtin_amdgcn_s_setreg(0x801, 0); }
 
 // Order LDS traffic between the lanes of one wavefront (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync()
@@ -143,11 +167,11 @@ __device__ __forceinline__ void load_enc_tile(u4_t (&R)[8], const uint8_t *__res
     if (nb == kEncTileBlocks) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            R[k] = *(const u4_t *)(src + k * 1024);
+            R[k] = ld_stream((const u4_t *)(src + k * 1024));
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            R[k] = 4 * k + (lane >> 4) < nb ? *(const u4_t *)(src + k * 1024) : u4_t{0, 0, 0, 0};
+            R[k] = 4 * k + (lane >> 4) < nb ? ld_stream((const u4_t *)(src + k * 1024)) : u4_t{0, 0, 0, 0};
     }
 }
 
@@ -185,22 +209,22 @@ __device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t la
             if (c < 2u * BITS * 16u) {
                 const u4_t val = *(const u4_t *)(stage + c * 16);
                 if (c < nchunks)
-                    *(u4_t *)(gdst + c * 16) = val;
+                    st_stream((u4_t *)(gdst + c * 16), val);
             }
         }
         if (blk < nb && half == 0)
-            norms[dst0 + blk] = n16;
+            st_stream(norms + dst0 + blk, n16);
     } else if (blk < nb) {
         const int64_t dst = cache_block(b0 + blk, row_blocks, cache_row_blocks, t0_blocks);
         const uint32_t *src = (const uint32_t *)(stage + blk * CB + GB * half);
         uint32_t *out = (uint32_t *)(codes + dst * CB + GB * half);
 #pragma unroll
         for (int k = 0; k < GW; ++k) {
-            out[k] = src[k];
-            out[2 * GW + k] = src[2 * GW + k];
+            st_stream(out + k, src[k]);
+            st_stream(out + 2 * GW + k, src[2 * GW + k]);
         }
         if (half == 0)
-            norms[dst] = n16;
+            st_stream(norms + dst, n16);
     }
 }
 
@@ -317,17 +341,18 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
             u[i + 32] = a - b;
         }
 
-        // 4. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F); the
+        // 4. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F).  The
         //    coefficients absorb 1/n and the clamp is scaled by n, so no division per
         //    value; g is odd, so a negated u[r] negates the last product.  n == 0
-        //    (zero block) gives F = 2^b/2 for every value.
+        //    (zero block) gives F = 2^b/2 for every value.  The last FMA adds 2^23 and
+        //    runs with float rounding toward -infinity, so its result is 2^23 + floor(F)
+        //    exactly and the code sits in the low mantissa bits (F stays in [0, 2^b)).
         const float rn = n > 0.0f ? __builtin_amdgcn_rcpf(n) : 0.0f;
         const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
         const float hi = cb.clamp_t * n, lo = -hi;
-        uint32_t wa[GW], wb[GW];   // groups r in [0, 32) and [32, 64)
-#pragma unroll
-        for (int k = 0; k < GW; ++k)
-            wa[k] = wb[k] = 0u;
+        constexpr float magic = 8388608.0f + mid;   // 2^23 + 2^b/2, exact
+        uint32_t fb[64];                             // bits of 2^23 + code
+        set_f32_round_down();
 #pragma unroll
         for (int r = 0; r < 64; ++r) {
             const float uc = __builtin_amdgcn_fmed3f(u[r], lo, hi);
@@ -337,16 +362,38 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
                 // g(t) = t * (g1 + g2 |t| + g3 t^2)
                 float p = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
                 p = __builtin_fmaf(__builtin_fabsf(uc), p, k1);
-                F = __builtin_fmaf(ui, p, mid);
+                F = __builtin_fmaf(ui, p, magic);
             } else {
-                F = __builtin_fmaf(ui, k1, mid);
+                F = __builtin_fmaf(ui, k1, magic);
             }
-            const uint32_t code = (uint32_t)F;
-            const int i = r & 31, bit = BITS * i, wi = bit >> 5, sh = bit & 31;
-            uint32_t *w = r < 32 ? wa : wb;
-            w[wi] |= code << sh;
-            if (sh + BITS > 32)
-                w[wi + 1] |= code >> (32 - sh);
+            fb[r] = __builtin_bit_cast(uint32_t, F);
+        }
+        set_f32_round_nearest();
+        // pack: 8 codes at a time by shift-and-add on the raw bits (the 2^23 exponent
+        // bits stay at bit 24 and above), then byte-splice the 8-code chunks into the
+        // LSB-first stream of each 32-code group
+        uint32_t wa[GW], wb[GW];   // groups r in [0, 32) and [32, 64)
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            uint32_t ch[4];
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int r0 = 32 * grp + 8 * qd;
+                uint32_t c = fb[r0 + 7];
+#pragma unroll
+                for (int i = 6; i >= 0; --i)
+                    c = lshl_add<BITS>(c, fb[r0 + i]);
+                ch[qd] = c;
+            }
+            uint32_t *w = grp ? wb : wa;
+            if constexpr (BITS == 3) {   // 24-bit chunks
+                w[0] = __builtin_amdgcn_perm(ch[1], ch[0], 0x04020100u);
+                w[1] = __builtin_amdgcn_perm(ch[2], ch[1], 0x05040201u);
+                w[2] = __builtin_amdgcn_perm(ch[3], ch[2], 0x06050402u);
+            } else {                     // 16-bit chunks
+                w[0] = __builtin_amdgcn_perm(ch[1], ch[0], 0x05040100u);
+                w[1] = __builtin_amdgcn_perm(ch[3], ch[2], 0x05040100u);
+            }
         }
 
         // 5. stage the packed groups at their place in the block (low lane: code bytes
@@ -387,13 +434,13 @@ __device__ __forceinline__ void load_codes(uint32_t (&W)[4 * BITS], uint16_t &N,
         const u4_t *in = (const u4_t *)(codes + src * (16 * BITS));
 #pragma unroll
         for (int k = 0; k < BITS; ++k) {
-            const u4_t c = in[k];
+            const u4_t c = ld_stream(in + k);
             W[4 * k] = c.x;
             W[4 * k + 1] = c.y;
             W[4 * k + 2] = c.z;
             W[4 * k + 3] = c.w;
         }
-        N = norms[src];
+        N = ld_stream(norms + src);
     } else {
 #pragma unroll
         for (int k = 0; k < 4 * BITS; ++k)
@@ -410,14 +457,14 @@ __device__ __forceinline__ void store_dec_tile(const uint8_t *lds, uint32_t lane
     if (nb == kBlocksPerWave) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
+            st_stream((u4_t *)(dst + k * 1024), *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)));
     } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const uint32_t blk = 4 * k + (lane >> 4);
             const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
             if (blk < nb)
-                *(u4_t *)(dst + k * 1024) = r;
+                st_stream((u4_t *)(dst + k * 1024), r);
         }
     }
 }
@@ -637,44 +684,41 @@ __global__ __launch_bounds__(256, 2) void qk_kernel(const uint8_t *__restrict__ 
     constexpr int LW = BITS;                             // 32-bit words per lane (32 codes)
     const uint32_t step = kWavesPerGroup * tpw;          // tokens between a wave's groups
 
-    // the codes and norm of this lane's slice of token t (zeros when not live)
-    auto fetch = [&](uint32_t t, uint32_t (&w)[LW], float &f) {
-        if (active && t < t_end) {
-            const size_t blk = (row0 + t) * m + slice;
-            const uint32_t *src = (const uint32_t *)(k_codes + blk * CB + part * (4 * BITS));
+    // The codes and raw norm of this lane's slice of token t.  Loads are issued
+    // unconditionally (rows past the chunk and padding lanes read a valid row and are
+    // zeroed when scored), so the prefetch is straight-line code.
+    const uint32_t sl = active ? slice : 0u;
+    auto fetch = [&](uint32_t t, uint32_t (&w)[LW], uint16_t &nr) {
+        const uint32_t tt = min(t, t_end - 1u);
+        const size_t blk = (row0 + tt) * m + sl;
+        const uint32_t *src = (const uint32_t *)(k_codes + blk * CB + part * (4 * BITS));
 #pragma unroll
-            for (int k = 0; k < LW; ++k)
-                w[k] = src[k];
-            f = (float)__builtin_bit_cast(_Float16, k_norms[blk]) * (1.0f / 128.0f);
-        } else {
-#pragma unroll
-            for (int k = 0; k < LW; ++k)
-                w[k] = 0u;
-            f = 0.0f;
-        }
+        for (int k = 0; k < LW; ++k)
+            w[k] = ld_stream(src + k);
+        nr = ld_stream(k_norms + blk);
     };
 
     uint32_t wn[kQkDepth][LW];
-    float fn[kQkDepth];
+    uint16_t nn[kQkDepth];
     uint32_t tb = t_begin + wave * tpw;   // first token of this wave's current group
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
-        fetch(tb + d * step + tok, wn[d], fn[d]);
+        fetch(tb + d * step + tok, wn[d], nn[d]);
     while (tb < t_end) {
         uint32_t wc[kQkDepth][LW];
-        float fc[kQkDepth];
+        uint16_t nc[kQkDepth];
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
 #pragma unroll
             for (int k = 0; k < LW; ++k)
                 wc[d][k] = wn[d][k];
-            fc[d] = fn[d];
+            nc[d] = nn[d];
         }
         const uint32_t tn = tb + kQkDepth * step;
         if (tn < t_end) {
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
-                fetch(tn + d * step + tok, wn[d], fn[d]);
+                fetch(tn + d * step + tok, wn[d], nn[d]);
         }
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
@@ -711,10 +755,13 @@ __global__ __launch_bounds__(256, 2) void qk_kernel(const uint8_t *__restrict__ 
                     }
                 }
             }
-            // per-slice norm (and the score scale), then sum the LPT lanes of the token
+            // per-slice norm and score scale (zero for padding lanes and rows past the
+            // chunk), then sum the LPT lanes of the token
+            const bool live = active && t < t_end;
+            const float f = live ? (float)__builtin_bit_cast(_Float16, nc[d]) * (scale * (1.0f / 128.0f)) : 0.0f;
 #pragma unroll
             for (int h = 0; h < GH; ++h)
-                acc[h] *= fc[d] * scale;
+                acc[h] *= f;
 #pragma unroll
             for (int h = 0; h < GH; ++h) {
                 acc[h] += dpp_f32<0xB1>(acc[h]);   // lane ^ 1 (quad_perm 1,0,3,2)
@@ -729,7 +776,7 @@ __global__ __launch_bounds__(256, 2) void qk_kernel(const uint8_t *__restrict__ 
 #pragma unroll
                 for (int h = 1; h < GH; ++h)
                     r = sub == (uint32_t)h ? acc[h] : r;
-                scores[((size_t)b * Hq + h0 + sub) * T + t] = r;
+                st_stream(scores + ((size_t)b * Hq + h0 + sub) * T + t, r);
             }
         }
         tb = tn;
@@ -782,7 +829,7 @@ int launch_encode(int bits, const void *x, int64_t nblocks, int64_t row_blocks,
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
-    static const int per_cu = groups_per_cu("TQ_ENCODE_GROUPS_PER_CU", 3);
+    static const int per_cu = groups_per_cu("TQ_ENCODE_GROUPS_PER_CU", 2);
     dim3 grid(grid_for(nblocks, kEncTileBlocks, per_cu)), block(256);
     if (bits == 3)
         hipLaunchKernelGGL(encode_kernel<3>, grid, block, 0, s, (const uint8_t *)x,
@@ -828,11 +875,12 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
         mp <<= 1;
         ++lpt_log2;
     }
-    // Rows per workgroup: enough workgroups to fill the chip several times over,
-    // whole rounds of kQkDepth groups per wave, at most 65535 row chunks.
+    // Rows per workgroup: about one round of workgroups (two per CU, the kernel's
+    // occupancy) so each pays its query-rotation prologue once, whole rounds of
+    // kQkDepth groups per wave, at most 65535 row chunks.
     const int64_t step = (int64_t)kWavesPerGroup * (64 >> lpt_log2) * kQkDepth;
     const int64_t pairs = B * Hkv * passes;
-    int64_t tpg = (T * pairs) / ((int64_t)cu_count() * 8);
+    int64_t tpg = (T * pairs + (int64_t)cu_count() * 2 - 1) / ((int64_t)cu_count() * 2);
     tpg = tpg < (T + 65534) / 65535 ? (T + 65534) / 65535 : tpg;
     tpg = ((tpg + step - 1) / step) * step;
     if (tpg < step)
