@@ -10,18 +10,21 @@
 // and the fused read that scores queries without materialising fp16 keys.
 //
 // Mapping on CDNA4 (wave64, 4 SIMDs x 16 lanes per CU, 160 KB LDS per CU):
-//  * encode / decode: one wavefront owns 64 consecutive blocks, one per lane.
-//    The 16 KB of fp16 values move between HBM and the wave with fully
-//    coalesced 16-byte accesses (every load / store instruction covers 1 KB
-//    contiguous) and are transposed through a wave-private, XOR-swizzled LDS
-//    tile, so each lane then holds a whole block and all seven butterfly
-//    stages run inside its registers with no cross-lane traffic.
+//  * encode / decode: a wavefront owns a tile of consecutive blocks (encode: 32
+//    blocks, two lanes per block; decode: 64 blocks, one per lane).  The fp16
+//    values move between HBM and the wave with fully coalesced 16-byte accesses
+//    (every load / store instruction covers 1 KB contiguous) and are transposed
+//    through a wave-private, XOR-swizzled LDS tile, so each lane then holds its
+//    values and the butterfly stages run inside its registers; the encoder's
+//    one cross-lane stage (span 64) is a v_permlane32_swap.
 //  * the first two butterfly stages of the encoder are done on the fp16
 //    inputs with v_dot2_f32_f16 against (1, 1) / (1, -1): exact products,
 //    float accumulation, the fp16 -> f32 conversion folded in.
-//  * the quantiser is one clamp, three FMAs and a float -> int conversion per
-//    value: an odd polynomial that crosses k exactly at the k-th positive
-//    threshold maps t to 2^b/2 + g(t), whose floor is the code.
+//  * the quantiser is one clamp and three FMAs per value (turbo2: one): an odd
+//    polynomial that crosses k exactly at the k-th positive threshold maps t to
+//    2^b/2 + g(t), whose floor is the code; the last FMA adds 2^23 under
+//    round-toward-minus-infinity, which leaves the floor in the low mantissa
+//    bits, and eight codes are then packed by seven shift-adds.
 //  * decode reads stage-one (turbo3) or stage-two (turbo2) outputs straight
 //    from a small LDS table indexed by 6 / 8 packed code bits.
 //  * q.K: q . (H y) = (H q) . y since H is symmetric, so each query slice is
@@ -58,15 +61,26 @@ __device__ __forceinline__ uint32_t swz(uint32_t blk, uint32_t chunk)
 // this compiler, so vector elements always go through a scalar first.
 __device__ __forceinline__ h2_t as_h2(uint32_t word) { return __builtin_bit_cast(h2_t, word); }
 
-// Streaming global accesses.  Each call touches every byte of its K/V values,
-// codes, norms and scores exactly once, so all of them carry the non-temporal
-// hint: loads do not allocate in the 256 MB memory-side cache (an allocation that
-// evicts a dirty line costs a write-back inside this kernel), and stores leave no
-// dirty lines there for the next kernel to write back.
+// Streaming global accesses.  Each call reads its inputs (fp16 K/V, codes, norms)
+// exactly once, so those loads carry the non-temporal hint: they do not allocate
+// in the 256 MB memory-side cache, where an allocation that evicts a dirty line
+// costs a write-back inside this kernel.  The encoder's codes and norms are read
+// back much later (by decode or q.K of later steps), so they are stored with the
+// hint too and leave no dirty lines behind.  Decoded fp16 values and scores are
+// consumed by the very next kernel (attention, softmax) and use plain stores,
+// which also stream large outputs at a higher rate than hinted stores do.
 template <class T>
 __device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
 template <class T>
 __device__ __forceinline__ void st_stream(T *p, T v) { __builtin_nontemporal_store(v, p); }
+
+// LDS by integer address (the byte offset in the workgroup's LDS).
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+template <class T>
+__device__ __forceinline__ T lds_load(uint32_t addr)
+{
+    return *(__attribute__((address_space(3))) const T *)(uintptr_t)addr;
+}
 
 // d = a.x * b.x + a.y * b.y + c in the three-operand VOP3P form (the compiler's
 // accumulate-in-place form would need a register copy per result here).
@@ -457,14 +471,14 @@ __device__ __forceinline__ void store_dec_tile(const uint8_t *lds, uint32_t lane
     if (nb == kBlocksPerWave) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            st_stream((u4_t *)(dst + k * 1024), *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)));
+            *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
     } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const uint32_t blk = 4 * k + (lane >> 4);
             const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
             if (blk < nb)
-                st_stream((u4_t *)(dst + k * 1024), r);
+                *(u4_t *)(dst + k * 1024) = r;
         }
     }
 }
@@ -593,193 +607,309 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
 }
 
 // ---------------------------------------------------------------- q.K scores
+//
+// scores[h, t] = scale * sum_j (n16[t, j] / 128) * (H q_j[h]) . y[t, j], y the
+// looked-up levels of key block j of cache row t.  Per kv head this is a
+// [query heads x 128] by [128 x tokens] contraction for every block j, done on the
+// matrix cores with v_mfma_f32_16x16x32_f16 (16 rows x 16 token columns, 32
+// products per row and column).
+//
+// Precision.  Operands are fp16, accumulation is float.  Each rotated query value
+// x is split into hi = fp16(x) and lo = fp16(x - hi), each codebook level y into
+// yh = fp16(y) and yl = fp16(y - yh).  Rows 0..7 of A carry the hi parts of up to
+// eight query heads, rows 8..15 their lo parts, and every value takes two products
+// of its column: x * yh and x * yl.  Row h plus row 8 + h is then
+// (hi + lo) . (yh + yl), x . y to about 2^-22 relative per term, plus float
+// accumulation.  x is the rotated query times scale / 128 times a power of two that
+// brings the head's largest |x| into [2^13, 2^14): no fp16 overflow and full fp16
+// precision for queries of any magnitude; the power is divided out at the end.
+//
+// Operand layout (the instruction's lanes: lane l holds row l % 16 of A and column
+// l % 16 of B, the same eight products 8 (l / 16) .. + 7 of both, and rows
+// 4 (l / 16) .. + 3 of column l % 16 of the result).  Lane l scores token l % 16
+// of a 16-token group; lane group p = l / 16 covers values [32 p, 32 p + 32) of
+// each 128-block, whose 32 codes are one 12-byte (turbo3) / 8-byte (turbo2) run of
+// the packed block.  Chunk c (0..7) of the run is values v0..v3 = 32 p + 4 c + 0..3
+// and fills the eight products as
+//   B: yh(v0) yh(v1) yl(v0) yl(v1) yh(v2) yh(v3) yl(v2) yl(v3)
+//   A:  x(v0)  x(v1)  x(v0)  x(v1)  x(v2)  x(v3)  x(v2)  x(v3)
+// so B is two 8-byte (hi pair, lo pair) entries of a 6-bit (two-value) LDS table
+// for turbo3, one 16-byte entry of an 8-bit (four-value) table for turbo2.
 
-// Token groups per wave whose codes are in flight while the previous groups are
-// scored (a group is the tokens one wave scores at once).
-constexpr int kQkDepth = 4;
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
 
-// BITS: 2 or 3.  GH: query heads per pass (1, 2 or 4).  LPT: lanes per key token
-// (4 * next power of two of m); lane = token * LPT + slice * 4 + part, the lane
-// covers values [32*part, 32*part + 32) of 128-block `slice` of the token.  A
+// (group, block) units whose codes are in flight while the previous ones are
+// scored; a group is the 16 tokens one wave scores at once.
+constexpr int kQkDepth = 8;
+constexpr int kQkHeads = 8;
+constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)   // query heads per pass
+constexpr int kQkTableBytes3 = 64 * 16 * 8;    // 64 entries x 16 copies x 8 B
+constexpr int kQkTableBytes2 = 256 * 8 * 16;   // 256 entries x 8 copies x 16 B
+constexpr int qk_table_bytes(int bits) { return bits == 3 ? kQkTableBytes3 : kQkTableBytes2; }
+// LDS of a workgroup: table | query operands [m][16 rows][128] fp16 | 8 floats
+inline size_t qk_smem_bytes(int bits, int64_t m)
+{
+    return (size_t)qk_table_bytes(bits) + (size_t)m * 16 * kBlock * 2 + kQkHeads * 4;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
+{
+    return __builtin_bit_cast(uint32_t, h2_t{a, b});
+}
+
+// x = hi + lo with hi = fp16(x), lo = fp16(x - hi) (x - hi is exact in float).
+__device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
+{
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
+
+// BITS: 2 or 3.  ONE_BLOCK: D == 128 (the query operands stay in registers).  A
 // workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head)
-// for GH query heads.
-template <int BITS, int GH>
-__global__ __launch_bounds__(256, 2) void qk_kernel(const uint8_t *__restrict__ k_codes,
+// for up to eight query heads (pass blockIdx.x % passes).
+template <int BITS, bool ONE_BLOCK>
+__global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *__restrict__ k_codes,
                                                     const uint16_t *__restrict__ k_norms,
                                                     const uint16_t *__restrict__ q,
                                                     float *__restrict__ scores, uint32_t Hkv,
                                                     int64_t Tc, uint32_t T, uint32_t m,
-                                                    uint32_t lpt_log2, uint32_t G, uint32_t Hq,
-                                                    uint32_t passes, uint32_t tpg, float scale,
-                                                    Codebook cb)
+                                                    uint32_t G, uint32_t Hq, uint32_t passes,
+                                                    uint32_t tpg, float scale, Codebook cb)
 {
-    // turbo3: 64 entries (two codes) -> (y0, y1); turbo2: 256 entries (four codes) ->
-    // y0..y3.  NC copies of the table interleaved entry by entry: copy c of entry e
-    // sits at (e * NC + c) * EW floats, and lane l reads copy l % NC, so the lanes
-    // one LDS cycle serves (16 lanes x 8 B, 8 lanes x 16 B) hit distinct banks
-    // whatever codes they look up.
-    constexpr int NE = BITS == 3 ? 64 : 256;
-    constexpr int EW = BITS == 3 ? 2 : 4;
-    constexpr int NC = BITS == 3 ? 16 : 8;
-    constexpr int kTableFloats = NE * EW * NC;
-    // one LDS buffer, the lookup table first (addressed by code bits alone), then
-    // the rotated query slices qs[head * m + slice][i]
-    __shared__ __attribute__((aligned(16))) float smem[kTableFloats + GH * 16 * kBlock];
-    float *table = smem;
-    float(*qs)[kBlock] = (float(*)[kBlock])(smem + kTableFloats);
+    extern __shared__ __attribute__((aligned(16))) uint8_t qk_smem[];
+    constexpr int NE = BITS == 3 ? 64 : 256;   // table entries
+    constexpr int EB = BITS == 3 ? 8 : 16;     // bytes per entry
+    constexpr int NC = BITS == 3 ? 16 : 8;     // copies: the lanes of one LDS cycle
+    constexpr int CB = 16 * BITS;              // code bytes per block
+    constexpr int LW = BITS;                   // code words per lane (32 codes)
+    static_assert(NC * EB == 128, "table entry stride is 2^7 bytes");
+    // Copy c of entry e sits at (e * NC + c) * EB and lane l reads copy l % NC, so the
+    // lanes served in one LDS cycle (16 x 8 B, 8 x 16 B) hit distinct banks whatever
+    // codes they look up.
+    uint8_t *table = qk_smem;
+    _Float16 *qa = (_Float16 *)(qk_smem + qk_table_bytes(BITS));   // [m][16][128]
+    float *pw_s = (float *)(qk_smem + qk_table_bytes(BITS) + (size_t)m * 16 * kBlock * 2);
 
     const uint32_t pass = blockIdx.x % passes;
     const uint32_t bg = blockIdx.x / passes;           // b * Hkv + g
     const uint32_t b = bg / Hkv, g = bg - b * Hkv;
-    const uint32_t h0 = g * G + pass * GH;             // first query head of this pass
-
-    for (int i = threadIdx.x; i < NE * NC; i += blockDim.x) {
-        const int e = i / NC;   // entry i / NC, copy i % NC
-        if constexpr (BITS == 3) {
-            table[2 * i] = cb.levels[e & 7];
-            table[2 * i + 1] = cb.levels[e >> 3];
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                table[4 * i + k] = cb.levels[(e >> (2 * k)) & 3];
-        }
-    }
-    // load the GH x m query slices as float, then rotate each in place
-    const uint32_t nvec = GH * m;
-    for (uint32_t i = threadIdx.x; i < nvec * kBlock; i += blockDim.x) {
-        uint32_t r = i / (m * kBlock), rest = i - r * (m * kBlock);
-        uint16_t hq = q[((size_t)b * Hq + h0 + r) * (m * kBlock) + rest];
-        qs[r * m + rest / kBlock][rest % kBlock] = (float)__builtin_bit_cast(_Float16, hq);
-    }
-    __syncthreads();
-    for (uint32_t h = 1; h < kBlock; h <<= 1) {
-        for (uint32_t p = threadIdx.x; p < nvec * (kBlock / 2); p += blockDim.x) {
-            uint32_t vec = p / (kBlock / 2), i = p % (kBlock / 2);
-            uint32_t j = (i / h) * 2 * h + (i % h);
-            float a = qs[vec][j], c = qs[vec][j + h];
-            qs[vec][j] = a + c;
-            qs[vec][j + h] = a - c;
-        }
-        __syncthreads();
-    }
+    const uint32_t h0 = g * G + pass * kQkHeads;       // first query head of this pass
+    const uint32_t nh = min(G - pass * kQkHeads, (uint32_t)kQkHeads);
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
-    const uint32_t lpt = 1u << lpt_log2, tpw = 64u >> lpt_log2;
-    const uint32_t tok = lane >> lpt_log2, sub = lane & (lpt - 1u);
-    const uint32_t slice = sub >> 2, part = sub & 3u;
-    const bool active = slice < m;
-    const float *tcopy = table + (lane % NC) * EW;   // this lane's table copy
-    float qr[GH][32];
-#pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            qr[h][i] = active ? qs[h * m + slice][32 * part + i] : 0.0f;
-
+    const uint32_t n = lane & 15u, part = lane >> 4;
     const uint32_t t_begin = blockIdx.y * tpg;
     const uint32_t t_end = min(T, t_begin + tpg);
-    const size_t row0 = (size_t)bg * Tc;                // first cache row of (b, g)
-    constexpr int CB = 16 * BITS;                        // code bytes per block
-    constexpr int LW = BITS;                             // 32-bit words per lane (32 codes)
-    const uint32_t step = kWavesPerGroup * tpw;          // tokens between a wave's groups
+    const size_t row0 = (size_t)bg * Tc;               // first cache row of (b, g)
 
-    // The codes and raw norm of this lane's slice of token t.  Loads are issued
-    // unconditionally (rows past the chunk and padding lanes read a valid row and are
-    // zeroed when scored), so the prefetch is straight-line code.
-    const uint32_t sl = active ? slice : 0u;
-    auto fetch = [&](uint32_t t, uint32_t (&w)[LW], uint16_t &nr) {
-        const uint32_t tt = min(t, t_end - 1u);
-        const size_t blk = (row0 + tt) * m + sl;
-        const uint32_t *src = (const uint32_t *)(k_codes + blk * CB + part * (4 * BITS));
+    // This wave's units: unit k is block k % m of group k / m, and group i covers
+    // tokens first + 64 i + [0, 16).
+    const uint32_t first = t_begin + wave * 16u;
+    const uint32_t ngroups = first < t_end ? (t_end - first + 63u) / 64u : 0u;
+    const uint32_t nunits = ngroups * m;
+
+    // Codes and raw norm of this lane's run of unit k.  Loads are unconditional (rows
+    // past the chunk read row t_end - 1 and are never stored), so the prefetch is
+    // straight-line code; the group's base address is wave-uniform (scalar) and each
+    // lane adds a 32-bit offset.
+    const uint32_t row_bytes = m * CB;
+    auto fetch = [&](uint32_t k, uint32_t (&w)[LW], uint16_t &nr) {
+        const uint32_t gi = ONE_BLOCK ? k : k / m;
+        const uint32_t j = ONE_BLOCK ? 0u : k - gi * m;
+        const uint32_t tb = min(first + gi * 64u, t_end - 1u);
+        const uint32_t r = min(n, t_end - 1u - tb);
+        const size_t blk0 = (row0 + tb) * m + j;
+        const uint32_t *src =
+            (const uint32_t *)(k_codes + blk0 * CB + (__umul24(r, row_bytes) + part * (4 * BITS)));
 #pragma unroll
-        for (int k = 0; k < LW; ++k)
-            w[k] = ld_stream(src + k);
-        nr = ld_stream(k_norms + blk);
+        for (int i = 0; i < LW; ++i)
+            w[i] = ld_stream(src + i);
+        nr = ld_stream((const uint16_t *)((const uint8_t *)(k_norms + blk0) + __umul24(r, 2u * m)));
     };
-
     uint32_t wn[kQkDepth][LW];
     uint16_t nn[kQkDepth];
-    uint32_t tb = t_begin + wave * tpw;   // first token of this wave's current group
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
-        fetch(tb + d * step + tok, wn[d], nn[d]);
-    while (tb < t_end) {
+        fetch(d, wn[d], nn[d]);
+
+    // lookup table of (yh, yl) pairs: entry e holds values e & 7, e >> 3 (turbo3) or
+    // (e >> 2 k) & 3 for k = 0..3 (turbo2), in the B order above
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * NC); i += blockDim.x) {
+        const uint32_t e = i / NC;
+        uint32_t *dst = (uint32_t *)(table + i * EB);
+        if constexpr (BITS == 3) {
+            _Float16 a0, a1, c0, c1;
+            split_f16(cb.levels[e & 7], a0, c0);
+            split_f16(cb.levels[e >> 3], a1, c1);
+            dst[0] = pack_h2(a0, a1);
+            dst[1] = pack_h2(c0, c1);
+        } else {
+            _Float16 a[4], c[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                split_f16(cb.levels[(e >> (2 * k)) & 3], a[k], c[k]);
+            dst[0] = pack_h2(a[0], a[1]);
+            dst[1] = pack_h2(c[0], c[1]);
+            dst[2] = pack_h2(a[2], a[3]);
+            dst[3] = pack_h2(c[2], c[3]);
+        }
+    }
+
+    // Query operands.  Wave w prepares heads w and w + 4: rotates every 128-slice
+    // (lane l holds positions l and 64 + l; span 64 in-lane, spans 32..1 across
+    // lanes), takes the head's largest |q'|, then writes x = q' * scale / 128 *
+    // 2^(14 - e) as hi (row hh) and lo (row 8 + hh).  Heads past nh get zero rows.
+    auto rotate = [&](const uint16_t *v, float &a, float &c) {
+        a = (float)__builtin_bit_cast(_Float16, v[lane]);
+        c = (float)__builtin_bit_cast(_Float16, v[64 + lane]);
+        const float s0 = a + c;
+        c = a - c;
+        a = s0;
+#pragma unroll
+        for (int h = 32; h >= 1; h >>= 1) {
+            const float pa = __shfl_xor(a, h, 64), pc = __shfl_xor(c, h, 64);
+            const bool up = (lane & (uint32_t)h) != 0u;
+            a = up ? pa - a : a + pa;
+            c = up ? pc - c : c + pc;
+        }
+    };
+    for (uint32_t hh = wave; hh < (uint32_t)kQkHeads; hh += kWavesPerGroup) {
+        _Float16 *hi_row = qa + hh * kBlock, *lo_row = qa + (kQkHeads + hh) * kBlock;
+        if (hh < nh) {
+            const uint16_t *qv = q + ((size_t)b * Hq + h0 + hh) * ((size_t)m * kBlock);
+            float mx = 0.0f, a1 = 0.0f, c1 = 0.0f;   // a1, c1: the single slice when m == 1
+            for (uint32_t j = 0; j < m; ++j) {
+                float a, c;
+                rotate(qv + j * kBlock, a, c);
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(c)));
+                a1 = a;
+                c1 = c;
+            }
+#pragma unroll
+            for (int h = 32; h >= 1; h >>= 1)
+                mx = __builtin_fmaxf(mx, __shfl_xor(mx, h, 64));
+            int e = 0;
+            (void)frexpf(mx * __builtin_fabsf(scale) * (1.0f / 128.0f), &e);
+            const float f = ldexpf(scale * (1.0f / 128.0f), 14 - e);
+            for (uint32_t j = 0; j < m; ++j) {
+                float a = a1, c = c1;
+                if (!ONE_BLOCK)
+                    rotate(qv + j * kBlock, a, c);
+                _Float16 ah, al, ch, cl;
+                split_f16(a * f, ah, al);
+                split_f16(c * f, ch, cl);
+                hi_row[j * 2048 + lane] = ah;
+                hi_row[j * 2048 + 64 + lane] = ch;
+                lo_row[j * 2048 + lane] = al;
+                lo_row[j * 2048 + 64 + lane] = cl;
+            }
+            if (lane == 0)
+                pw_s[hh] = ldexpf(1.0f, e - 14);
+        } else {
+            for (uint32_t j = 0; j < m; ++j) {
+                hi_row[j * 2048 + lane] = hi_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
+                lo_row[j * 2048 + lane] = lo_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
+            }
+            if (lane == 0)
+                pw_s[hh] = 0.0f;
+        }
+    }
+    __syncthreads();
+
+    // A operands of block j for this lane's row (lane % 16) and value run
+    const _Float16 *arow = qa + n * kBlock + part * 32;
+    auto load_a = [&](uint32_t j, h8_t (&A)[8]) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t *p = (const uint32_t *)(arow + j * 2048 + 4 * c);
+            const uint32_t x01 = p[0], x23 = p[1];
+            A[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
+        }
+    };
+    h8_t A[8];
+    if constexpr (ONE_BLOCK)
+        load_a(0, A);
+    // LDS address of this lane's table copy (entries are addressed as integers so that
+    // each lookup is one bit-field extract and one shift-add)
+    const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)table + (lane % NC) * EB;
+    // after the hi/lo combine, lane l holds query heads hu and hu + 2 of token l % 16
+    const uint32_t hu = 4u * (part & 1u) + (lane >> 5);
+    const float pw_u = pw_s[hu], pw_v = pw_s[hu + 2];
+    float* const out_u = scores + ((size_t)b * Hq + h0 + hu) * T;
+    float* const out_v = scores + ((size_t)b * Hq + h0 + hu + 2) * T;
+
+    f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (uint32_t k0 = 0; k0 < nunits; k0 += kQkDepth) {
         uint32_t wc[kQkDepth][LW];
         uint16_t nc[kQkDepth];
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
 #pragma unroll
-            for (int k = 0; k < LW; ++k)
-                wc[d][k] = wn[d][k];
+            for (int i = 0; i < LW; ++i)
+                wc[d][i] = wn[d][i];
             nc[d] = nn[d];
         }
-        const uint32_t tn = tb + kQkDepth * step;
-        if (tn < t_end) {
+        if (k0 + kQkDepth < nunits) {
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
-                fetch(tn + d * step + tok, wn[d], nn[d]);
+                fetch(k0 + kQkDepth + d, wn[d], nn[d]);
         }
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
-            const uint32_t t = tb + d * step + tok;
+            const uint32_t k = k0 + d;
+            const uint32_t gi = ONE_BLOCK ? k : k / m;
+            const uint32_t j = ONE_BLOCK ? 0u : k - gi * m;
+            if constexpr (!ONE_BLOCK)
+                load_a(j, A);
             const uint32_t *w = wc[d];
-            float acc[GH];
+            // two accumulation chains (even / odd chunks) halve the dependent MFMA latency
+            f4_t D[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int h = 0; h < GH; ++h)
-                acc[h] = 0.0f;
-            if constexpr (BITS == 3) {
+            for (int c = 0; c < 8; ++c) {
+                u4_t bv;
+                if constexpr (BITS == 3) {
+                    uint32_t o[2];   // LDS byte offsets of the two entries
 #pragma unroll
-                for (int p = 0; p < 16; ++p) {
-                    const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
-                    uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
-                                          : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-                    float2 y = *(const float2 *)(tcopy + e * (NC * EW));
-#pragma unroll
-                    for (int h = 0; h < GH; ++h) {
-                        acc[h] = __builtin_fmaf(qr[h][2 * p], y.x, acc[h]);
-                        acc[h] = __builtin_fmaf(qr[h][2 * p + 1], y.y, acc[h]);
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        const int bit = 12 * c + 6 * k2, wi = bit >> 5, sh = bit & 31;
+                        const uint32_t e = sh <= 26
+                                               ? __builtin_amdgcn_ubfe(w[wi], sh, 6)
+                                               : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
+                        o[k2] = lshl_add<7>(e, tcopy);   // e * NC * EB + copy
                     }
+                    const uint64_t r0 = lds_load<uint64_t>(o[0]), r1 = lds_load<uint64_t>(o[1]);
+                    bv = u4_t{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)};
+                } else {
+                    const uint32_t e = __builtin_amdgcn_ubfe(w[c >> 2], 8 * (c & 3), 8);
+                    bv = lds_load<u4_t>(lshl_add<7>(e, tcopy));
                 }
-            } else {
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
-                    float4 y = *(const float4 *)(tcopy + e * (NC * EW));
-#pragma unroll
-                    for (int h = 0; h < GH; ++h) {
-                        acc[h] = __builtin_fmaf(qr[h][4 * p], y.x, acc[h]);
-                        acc[h] = __builtin_fmaf(qr[h][4 * p + 1], y.y, acc[h]);
-                        acc[h] = __builtin_fmaf(qr[h][4 * p + 2], y.z, acc[h]);
-                        acc[h] = __builtin_fmaf(qr[h][4 * p + 3], y.w, acc[h]);
-                    }
+                D[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], __builtin_bit_cast(h8_t, bv),
+                                                                  D[c & 1], 0, 0, 0);
+            }
+            const float nf = (float)__builtin_bit_cast(_Float16, nc[d]);
+            if constexpr (ONE_BLOCK)
+                acc = (D[0] + D[1]) * nf;
+            else
+                acc += (D[0] + D[1]) * nf;
+            if (ONE_BLOCK || j == m - 1u) {
+                // rows h (hi) and 8 + h (lo) sit in lanes l and l + 32: one swap pairs them
+                float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
+                swap32(s0, s1);
+                swap32(s2, s3);
+                const float u = (s0 + s1) * pw_u, v = (s2 + s3) * pw_v;
+                const uint32_t t = first + gi * 64u + n;
+                if (t < t_end) {
+                    if (hu < nh)
+                        out_u[t] = u;
+                    if (hu + 2u < nh)
+                        out_v[t] = v;
                 }
-            }
-            // per-slice norm and score scale (zero for padding lanes and rows past the
-            // chunk), then sum the LPT lanes of the token
-            const bool live = active && t < t_end;
-            const float f = live ? (float)__builtin_bit_cast(_Float16, nc[d]) * (scale * (1.0f / 128.0f)) : 0.0f;
-#pragma unroll
-            for (int h = 0; h < GH; ++h)
-                acc[h] *= f;
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                acc[h] += dpp_f32<0xB1>(acc[h]);   // lane ^ 1 (quad_perm 1,0,3,2)
-                acc[h] += dpp_f32<0x4E>(acc[h]);   // lane ^ 2 (quad_perm 2,3,0,1)
-            }
-            for (uint32_t sft = 4; sft < lpt; sft <<= 1)
-#pragma unroll
-                for (int h = 0; h < GH; ++h)
-                    acc[h] += __shfl_xor(acc[h], (int)sft, 64);
-            if (t < t_end && sub < GH) {
-                float r = acc[0];
-#pragma unroll
-                for (int h = 1; h < GH; ++h)
-                    r = sub == (uint32_t)h ? acc[h] : r;
-                st_stream(scores + ((size_t)b * Hq + h0 + sub) * T + t, r);
+                if constexpr (!ONE_BLOCK)
+                    acc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
-        tb = tn;
     }
 }
 
@@ -800,7 +930,7 @@ int cu_count()
 }
 
 // Workgroups per compute unit of a persistent grid: the kernel's own occupancy
-// (encode: three 4-wave groups, at most 168 VGPRs per lane and 3 x 32 KB of LDS;
+// (encode: two 4-wave groups, at most 168 VGPRs per lane and 2 x 38 KB of LDS;
 // decode: two groups, 2 x 64 KB of LDS and at most 256 VGPRs per lane),
 // overridable for tuning sweeps with
 // TQ_ENCODE_GROUPS_PER_CU / TQ_DECODE_GROUPS_PER_CU.
@@ -868,19 +998,14 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
     const int64_t G = Hq / Hkv;
-    const int GH = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-    const int64_t passes = G / GH;
-    uint32_t mp = 1, lpt_log2 = 2;
-    while (mp < (uint32_t)m) {
-        mp <<= 1;
-        ++lpt_log2;
-    }
-    // Rows per workgroup: about one round of workgroups (two per CU, the kernel's
-    // occupancy) so each pays its query-rotation prologue once, whole rounds of
-    // kQkDepth groups per wave, at most 65535 row chunks.
-    const int64_t step = (int64_t)kWavesPerGroup * (64 >> lpt_log2) * kQkDepth;
+    const int64_t passes = (G + kQkHeads - 1) / kQkHeads;
+    // Rows per workgroup: about one round of workgroups (kQkGroupsPerCu per CU, the
+    // kernel's occupancy) so each pays its table and query prologue once, whole
+    // batches of kQkDepth units per wave, at most 65535 row chunks.
+    const int64_t step = (int64_t)kWavesPerGroup * 16 * (m >= kQkDepth ? 1 : kQkDepth / m);
     const int64_t pairs = B * Hkv * passes;
-    int64_t tpg = (T * pairs + (int64_t)cu_count() * 2 - 1) / ((int64_t)cu_count() * 2);
+    const int64_t round = (int64_t)cu_count() * kQkGroupsPerCu;
+    int64_t tpg = (T * pairs + round - 1) / round;
     tpg = tpg < (T + 65534) / 65535 ? (T + 65534) / 65535 : tpg;
     tpg = ((tpg + step - 1) / step) * step;
     if (tpg < step)
@@ -891,22 +1016,23 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
         tpg = (((T + 65534) / 65535 + step - 1) / step) * step;
     dim3 grid((uint32_t)pairs, (uint32_t)((T + tpg - 1) / tpg));
     dim3 block(256);
-#define TQ_QK_LAUNCH(BB, GG)                                                                    \
-    hipLaunchKernelGGL((qk_kernel<BB, GG>), grid, block, 0, s, (const uint8_t *)k_codes,        \
-                       (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,   \
-                       Tc, (uint32_t)T, (uint32_t)m, lpt_log2, (uint32_t)G, (uint32_t)Hq,      \
-                       (uint32_t)passes, (uint32_t)tpg, scale, *cb)
-    if (bits == 3) {
-        if (GH == 4) TQ_QK_LAUNCH(3, 4);
-        else if (GH == 2) TQ_QK_LAUNCH(3, 2);
-        else TQ_QK_LAUNCH(3, 1);
-    } else {
-        if (GH == 4) TQ_QK_LAUNCH(2, 4);
-        else if (GH == 2) TQ_QK_LAUNCH(2, 2);
-        else TQ_QK_LAUNCH(2, 1);
-    }
-#undef TQ_QK_LAUNCH
-    return (int)hipGetLastError();
+    const size_t smem = qk_smem_bytes(bits, m);
+    auto launch = [&](auto kern) -> int {
+        if (smem > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess)
+                return (int)e;
+        }
+        hipLaunchKernelGGL(kern, grid, block, smem, s, (const uint8_t *)k_codes,
+                           (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,
+                           Tc, (uint32_t)T, (uint32_t)m, (uint32_t)G, (uint32_t)Hq,
+                           (uint32_t)passes, (uint32_t)tpg, scale, *cb);
+        return (int)hipGetLastError();
+    };
+    if (bits == 3)
+        return m == 1 ? launch(qk_kernel<3, true>) : launch(qk_kernel<3, false>);
+    return m == 1 ? launch(qk_kernel<2, true>) : launch(qk_kernel<2, false>);
 }
 
 }  // namespace tq
