@@ -151,11 +151,14 @@ def test_append_leaves_other_rows(bits):
     check_norms(norms[:, :, Tc - 1].cpu().numpy(), on, tok.numpy(), "append")
 
 
-def _qk_case(bits, B, Hkv, G, Tc, T, D, seed):
+def _qk_case(bits, B, Hkv, G, Tc, T, D, seed, q_mul=None, scale=None):
     k = _rand_kv(seed, B, Hkv, Tc, D)
     codes, norms = _gpu_encode(bits, k, Tc, 0)
     q = gen.queries(seed + 1, B, Hkv * G, D)
-    scale = 1.0 / math.sqrt(D)
+    if q_mul is not None:   # per-head magnitudes, [Hq] factors
+        q = (q.double() * torch.as_tensor(q_mul, dtype=torch.float64)[None, :, None]).half()
+        assert bool(torch.isfinite(q).all())
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     scores = torch.empty((B, Hkv * G, T), dtype=torch.float32, device="cuda")
     tq.tq_qk_scores(bits, codes, norms, q.cuda(), scale, scores)
     torch.cuda.synchronize()
@@ -165,7 +168,7 @@ def _qk_case(bits, B, Hkv, G, Tc, T, D, seed):
     kn = np.linalg.norm(khat, axis=-1)                                  # [B, Hkv, T]
     qn = np.linalg.norm(q.numpy().astype(np.float64), axis=-1)         # [B, Hq]
     knh = np.repeat(kn, G, axis=1)                                      # head h reads kv h // G
-    return check_scores(scores.cpu().numpy(), ref, qn[:, :, None] * scale, knh,
+    return check_scores(scores.cpu().numpy(), ref, qn[:, :, None] * abs(scale), knh,
                         f"qk bits={bits} B={B} Hkv={Hkv} G={G} T={T} D={D}")
 
 
@@ -173,11 +176,25 @@ def _qk_case(bits, B, Hkv, G, Tc, T, D, seed):
 @pytest.mark.parametrize("case", [
     (2, 2, 4, 100, 97, 128),     # GQA group 4, ragged T < Tc
     (1, 3, 1, 70, 70, 128),      # no grouping
-    (2, 1, 8, 40, 33, 128),      # group 8: two passes of four heads
+    (2, 1, 8, 40, 33, 128),      # group 8: one full pass of eight heads
+    (1, 1, 12, 40, 40, 128),     # group 12: passes of eight and four heads
+    (1, 1, 16, 64, 61, 128),     # group 16: two full passes
     (1, 2, 3, 50, 50, 256),      # odd group, head_dim 256
-    (1, 1, 2, 1100, 1100, 384),  # three blocks per row (lanes padded to 16), two token chunks
+    (1, 1, 2, 1100, 1100, 384),  # three blocks per row, several token chunks
     (1, 2, 5, 20, 17, 1024),     # eight blocks per row
+    (1, 1, 2, 24, 21, 2048),     # sixteen blocks per row (largest head_dim, 96 KB of LDS for turbo2)
+    (1, 2, 4, 5000, 4999, 128),  # many token chunks and waves, ragged last group
 ])
 def test_qk_scores(bits, case):
     B, Hkv, G, Tc, T, D = case
     print(_qk_case(bits, B, Hkv, G, Tc, T, D, seed=31 + D + G))
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_qk_query_magnitudes(bits):
+    """Query heads from 1e-4 to 3e3 times N(0, 1) in one call (fp16 subnormals at the
+    small end), and a negative scale: every head keeps the 2e-3 relative bound, so the
+    per-head fp16 operand scaling holds whatever the query's magnitude."""
+    mul = [1e-4, 3e-3, 1.0, 40.0, 3e3, 0.5, 1e-2, 7.0]
+    print(_qk_case(bits, 1, 2, 4, 300, 300, 128, seed=77, q_mul=mul))
+    print(_qk_case(bits, 1, 1, 3, 64, 64, 256, seed=78, scale=-0.37))
