@@ -82,6 +82,11 @@ __device__ __forceinline__ T lds_load(uint32_t addr)
     return *(__attribute__((address_space(3))) const T *)(uintptr_t)addr;
 }
 
+// Lookup tables of 8-byte entries are replicated kLdsCopies8 times: the LDS serves
+// 256 bytes (32 lanes x 8 B) per cycle from 64 banks, so the 32 lanes of one cycle,
+// each reading its own copy, never collide whatever entries they pick.
+constexpr int kLdsCopies8 = 32;
+
 // d = a.x * b.x + a.y * b.y + c in the three-operand VOP3P form (the compiler's
 // accumulate-in-place form would need a register copy per result here).
 // fp16 x (+-1) products are exact, the sum is a float.
@@ -491,34 +496,23 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
                                                         int64_t t0_blocks,
                                                         uint8_t *__restrict__ x, Codebook cb)
 {
-    // turbo3: 64 entries (6 code bits = two codes) -> stage-one outputs (y0+y1, y0-y1)
-    // turbo2: 256 entries (8 code bits = four codes) -> stage-two outputs
-    constexpr int NE = BITS == 3 ? 64 : 256;
-    constexpr int EW = BITS == 3 ? 2 : 4;
-    constexpr int kTableBytes = NE * EW * 4;
-    // one LDS buffer, the table first: its entries are then addressed by the
-    // extracted code bits alone (the 16-bit instruction offset cannot reach past
-    // the 64 KB of tiles)
+    // Entry e (2 b code bits = two codes, the first in the low bits) -> stage-one
+    // outputs (y0 + y1, y0 - y1); 64 entries for turbo3, 16 for turbo2, each
+    // replicated kLdsCopies8 times so that the 32 lanes of one LDS cycle never
+    // collide (copy c of entry e at (e * 32 + c) * 8, lane l reads copy l % 32).
+    constexpr int NE = 1 << (2 * BITS);
+    constexpr int kTableBytes = NE * kLdsCopies8 * 8;
+    // one LDS buffer, the table first
     __shared__ __attribute__((aligned(16))) uint8_t smem[kTableBytes + kWavesPerGroup * kTileBytes];
-    float *table = (float *)smem;
-    for (int e = threadIdx.x; e < NE; e += blockDim.x) {
-        if constexpr (BITS == 3) {
-            float y0 = cb.levels[e & 7], y1 = cb.levels[e >> 3];
-            table[2 * e] = y0 + y1;
-            table[2 * e + 1] = y0 - y1;
-        } else {
-            float y0 = cb.levels[e & 3], y1 = cb.levels[(e >> 2) & 3];
-            float y2 = cb.levels[(e >> 4) & 3], y3 = cb.levels[e >> 6];
-            float s0 = y0 + y1, s1 = y0 - y1, s2 = y2 + y3, s3 = y2 - y3;
-            table[4 * e] = s0 + s2;
-            table[4 * e + 1] = s1 + s3;
-            table[4 * e + 2] = s0 - s2;
-            table[4 * e + 3] = s1 - s3;
-        }
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += blockDim.x) {
+        const uint32_t e = i / kLdsCopies8;
+        const float y0 = cb.levels[e & ((1u << BITS) - 1u)], y1 = cb.levels[e >> BITS];
+        *(float2 *)(smem + i * 8) = float2{y0 + y1, y0 - y1};
     }
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)smem + (lane % kLdsCopies8) * 8;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
     const uint32_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
     const uint32_t stride = gridDim.x * kWavesPerGroup;
@@ -553,29 +547,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
                              row_blocks, cache_row_blocks, t0_blocks);
 
         float u[kBlock];
-        if constexpr (BITS == 3) {
 #pragma unroll
-            for (int p = 0; p < 64; ++p) {
-                const int bit = 6 * p, wi = bit >> 5, sh = bit & 31;
-                uint32_t e = sh <= 26 ? (w[wi] >> sh) & 63u
-                                      : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-                float2 t = *(const float2 *)(table + 2 * e);
-                u[2 * p] = t.x;
-                u[2 * p + 1] = t.y;
-            }
-            fwht_from<2, 64>(u);
-        } else {
-#pragma unroll
-            for (int p = 0; p < 32; ++p) {
-                uint32_t e = (w[p >> 2] >> (8 * (p & 3))) & 255u;
-                float4 t = *(const float4 *)(table + 4 * e);
-                u[4 * p] = t.x;
-                u[4 * p + 1] = t.y;
-                u[4 * p + 2] = t.z;
-                u[4 * p + 3] = t.w;
-            }
-            fwht_from<4, 64>(u);
+        for (int p = 0; p < 64; ++p) {
+            constexpr int FB = 2 * BITS;   // index bits: two codes
+            const int bit = FB * p, wi = bit >> 5, sh = bit & 31;
+            const uint32_t e = sh <= 32 - FB ? __builtin_amdgcn_ubfe(w[wi], sh, FB)
+                                             : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & (NE - 1u);
+            const uint64_t t = lds_load<uint64_t>(lshl_add<8>(e, tcopy));
+            u[2 * p] = __builtin_bit_cast(float, (uint32_t)t);
+            u[2 * p + 1] = __builtin_bit_cast(float, (uint32_t)(t >> 32));
         }
+        fwht_from<2, 64>(u);
         // last stage with the rescale by n16/128 folded in: (a +- b) s = a s +- b s
 #pragma unroll
         for (int j = 0; j < 64; ++j) {
@@ -633,8 +615,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
 // and fills the eight products as
 //   B: yh(v0) yh(v1) yl(v0) yl(v1) yh(v2) yh(v3) yl(v2) yl(v3)
 //   A:  x(v0)  x(v1)  x(v0)  x(v1)  x(v2)  x(v3)  x(v2)  x(v3)
-// so B is two 8-byte (hi pair, lo pair) entries of a 6-bit (two-value) LDS table
-// for turbo3, one 16-byte entry of an 8-bit (four-value) table for turbo2.
+// so B is two 8-byte (hi pair, lo pair) entries of a two-value LDS table indexed by
+// 6 code bits for turbo3, one 16-byte entry of a four-value table indexed by 8 code
+// bits for turbo2.
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -644,9 +627,11 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 constexpr int kQkDepth = 8;
 constexpr int kQkHeads = 8;
 constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)   // query heads per pass
-constexpr int kQkTableBytes3 = 64 * 16 * 8;    // 64 entries x 16 copies x 8 B
-constexpr int kQkTableBytes2 = 256 * 8 * 16;   // 256 entries x 8 copies x 16 B
-constexpr int qk_table_bytes(int bits) { return bits == 3 ? kQkTableBytes3 : kQkTableBytes2; }
+// turbo3: 64 two-value entries of 8 B, kLdsCopies8 copies (conflict-free);
+// turbo2: 256 four-value entries of 16 B, 8 copies (16 B lookups are served 16 lanes
+// per cycle, so lanes l and l + 8 may meet: the full 16 copies would take 64 KB and
+// halve the workgroups per CU, which costs more than the conflicts).
+constexpr int qk_table_bytes(int bits) { return bits == 3 ? 64 * kLdsCopies8 * 8 : 256 * 8 * 16; }
 // LDS of a workgroup: table | query operands [m][16 rows][128] fp16 | 8 floats
 inline size_t qk_smem_bytes(int bits, int64_t m)
 {
@@ -678,15 +663,15 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                                                     uint32_t tpg, float scale, Codebook cb)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t qk_smem[];
-    constexpr int NE = BITS == 3 ? 64 : 256;   // table entries
+    constexpr int NE = BITS == 3 ? 64 : 256;   // table entries (two / four codes)
     constexpr int EB = BITS == 3 ? 8 : 16;     // bytes per entry
-    constexpr int NC = BITS == 3 ? 16 : 8;     // copies: the lanes of one LDS cycle
+    constexpr int NC = BITS == 3 ? kLdsCopies8 : 8;   // copies
+    constexpr int ES = BITS == 3 ? 8 : 7;      // log2 of the entry stride NC * EB
     constexpr int CB = 16 * BITS;              // code bytes per block
     constexpr int LW = BITS;                   // code words per lane (32 codes)
-    static_assert(NC * EB == 128, "table entry stride is 2^7 bytes");
-    // Copy c of entry e sits at (e * NC + c) * EB and lane l reads copy l % NC, so the
-    // lanes served in one LDS cycle (16 x 8 B, 8 x 16 B) hit distinct banks whatever
-    // codes they look up.
+    static_assert(NC * EB == (1 << ES), "entry stride");
+    static_assert(NE * NC * EB == qk_table_bytes(BITS), "table size");
+    // Copy c of entry e sits at (e * NC + c) * EB and lane l reads copy l % NC.
     uint8_t *table = qk_smem;
     _Float16 *qa = (_Float16 *)(qk_smem + qk_table_bytes(BITS));   // [m][16][128]
     float *pw_s = (float *)(qk_smem + qk_table_bytes(BITS) + (size_t)m * 16 * kBlock * 2);
@@ -704,21 +689,26 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     const uint32_t t_end = min(T, t_begin + tpg);
     const size_t row0 = (size_t)bg * Tc;               // first cache row of (b, g)
 
-    // This wave's units: unit k is block k % m of group k / m, and group i covers
-    // tokens first + 64 i + [0, 16).
-    const uint32_t first = t_begin + wave * 16u;
-    const uint32_t ngroups = first < t_end ? (t_end - first + 63u) / 64u : 0u;
+    // This wave's units: the wave owns the contiguous rows [first, last) of the
+    // chunk; unit k is block k % m of group k / m, and group i covers rows
+    // first + 16 i + [0, 16).  Contiguous rows keep each wave's reads, norm lines and
+    // score lines to itself.
+    const uint32_t wspan = tpg / kWavesPerGroup;
+    const uint32_t first = t_begin + wave * wspan;
+    const uint32_t last = min(t_end, first + wspan);
+    const uint32_t ngroups = first < last ? (last - first + 15u) / 16u : 0u;
     const uint32_t nunits = ngroups * m;
 
     // Codes and raw norm of this lane's run of unit k.  Loads are unconditional (rows
-    // past the chunk read row t_end - 1 and are never stored), so the prefetch is
+    // past the wave's range read valid rows of the chunk, at most row t_end - 1, and
+    // are never stored), so the prefetch is
     // straight-line code; the group's base address is wave-uniform (scalar) and each
     // lane adds a 32-bit offset.
     const uint32_t row_bytes = m * CB;
     auto fetch = [&](uint32_t k, uint32_t (&w)[LW], uint16_t &nr) {
         const uint32_t gi = ONE_BLOCK ? k : k / m;
         const uint32_t j = ONE_BLOCK ? 0u : k - gi * m;
-        const uint32_t tb = min(first + gi * 64u, t_end - 1u);
+        const uint32_t tb = min(first + gi * 16u, t_end - 1u);
         const uint32_t r = min(n, t_end - 1u - tb);
         const size_t blk0 = (row0 + tb) * m + j;
         const uint32_t *src =
@@ -726,34 +716,45 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 #pragma unroll
         for (int i = 0; i < LW; ++i)
             w[i] = ld_stream(src + i);
-        nr = ld_stream((const uint16_t *)((const uint8_t *)(k_norms + blk0) + __umul24(r, 2u * m)));
+        if constexpr (!ONE_BLOCK)
+            nr = ld_stream((const uint16_t *)((const uint8_t *)(k_norms + blk0) + __umul24(r, 2u * m)));
+    };
+    // D == 128: the norms of a whole batch (kQkDepth groups = 128 contiguous rows) come
+    // in two loads, rows first + 16 k + lane and + 64, and each unit takes its row's
+    // norm from the lane that holds it; a separate small load per unit would cost the
+    // memory pipeline about as much as the unit's codes.
+    static_assert(!ONE_BLOCK || kQkDepth * 16 == 128, "two norm loads per batch");
+    auto fetch_norms = [&](uint32_t k, uint32_t &na, uint32_t &nb) {
+        const uint32_t ta = min(first + 16u * k + lane, t_end - 1u);
+        const uint32_t tb = min(first + 16u * k + 64u + lane, t_end - 1u);
+        na = ld_stream(k_norms + row0 + ta);
+        nb = ld_stream(k_norms + row0 + tb);
     };
     uint32_t wn[kQkDepth][LW];
     uint16_t nn[kQkDepth];
+    uint32_t nna = 0, nnb = 0;
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
         fetch(d, wn[d], nn[d]);
+    if constexpr (ONE_BLOCK)
+        fetch_norms(0, nna, nnb);
 
-    // lookup table of (yh, yl) pairs: entry e holds values e & 7, e >> 3 (turbo3) or
-    // (e >> 2 k) & 3 for k = 0..3 (turbo2), in the B order above
+    // lookup table of (yh, yl) pairs in the B order above: entry e holds the values
+    // of codes e & 7, e >> 3 (turbo3) or (e >> 2 k) & 3, k = 0..3 (turbo2)
     for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * NC); i += blockDim.x) {
         const uint32_t e = i / NC;
-        uint32_t *dst = (uint32_t *)(table + i * EB);
         if constexpr (BITS == 3) {
             _Float16 a0, a1, c0, c1;
             split_f16(cb.levels[e & 7], a0, c0);
             split_f16(cb.levels[e >> 3], a1, c1);
-            dst[0] = pack_h2(a0, a1);
-            dst[1] = pack_h2(c0, c1);
+            *(uint2 *)(table + i * EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         } else {
             _Float16 a[4], c[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 split_f16(cb.levels[(e >> (2 * k)) & 3], a[k], c[k]);
-            dst[0] = pack_h2(a[0], a[1]);
-            dst[1] = pack_h2(c[0], c[1]);
-            dst[2] = pack_h2(a[2], a[3]);
-            dst[3] = pack_h2(c[2], c[3]);
+            *(uint4 *)(table + i * EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
+                                                pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
         }
     }
 
@@ -851,10 +852,13 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                 wc[d][i] = wn[d][i];
             nc[d] = nn[d];
         }
+        const uint32_t nca = nna, ncb = nnb;
         if (k0 + kQkDepth < nunits) {
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
                 fetch(k0 + kQkDepth + d, wn[d], nn[d]);
+            if constexpr (ONE_BLOCK)
+                fetch_norms(k0 + kQkDepth, nna, nnb);
         }
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
@@ -870,25 +874,28 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             for (int c = 0; c < 8; ++c) {
                 u4_t bv;
                 if constexpr (BITS == 3) {
-                    uint32_t o[2];   // LDS byte offsets of the two entries
+                    uint32_t o[2];   // LDS addresses of the entries of v0 v1 and v2 v3
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2) {
                         const int bit = 12 * c + 6 * k2, wi = bit >> 5, sh = bit & 31;
                         const uint32_t e = sh <= 26
                                                ? __builtin_amdgcn_ubfe(w[wi], sh, 6)
                                                : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-                        o[k2] = lshl_add<7>(e, tcopy);   // e * NC * EB + copy
+                        o[k2] = lshl_add<ES>(e, tcopy);   // e * NC * EB + copy
                     }
                     const uint64_t r0 = lds_load<uint64_t>(o[0]), r1 = lds_load<uint64_t>(o[1]);
                     bv = u4_t{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)};
                 } else {
                     const uint32_t e = __builtin_amdgcn_ubfe(w[c >> 2], 8 * (c & 3), 8);
-                    bv = lds_load<u4_t>(lshl_add<7>(e, tcopy));
+                    bv = lds_load<u4_t>(lshl_add<ES>(e, tcopy));
                 }
                 D[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], __builtin_bit_cast(h8_t, bv),
                                                                   D[c & 1], 0, 0, 0);
             }
-            const float nf = (float)__builtin_bit_cast(_Float16, nc[d]);
+            uint16_t nr16 = nc[d];
+            if constexpr (ONE_BLOCK)
+                nr16 = (uint16_t)__shfl((int)(d < 4 ? nca : ncb), 16 * (d & 3) + (int)n, 64);
+            const float nf = (float)__builtin_bit_cast(_Float16, nr16);
             if constexpr (ONE_BLOCK)
                 acc = (D[0] + D[1]) * nf;
             else
@@ -899,8 +906,8 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                 swap32(s0, s1);
                 swap32(s2, s3);
                 const float u = (s0 + s1) * pw_u, v = (s2 + s3) * pw_v;
-                const uint32_t t = first + gi * 64u + n;
-                if (t < t_end) {
+                const uint32_t t = first + gi * 16u + n;
+                if (t < last) {
                     if (hu < nh)
                         out_u[t] = u;
                     if (hu + 2u < nh)
@@ -931,7 +938,7 @@ int cu_count()
 
 // Workgroups per compute unit of a persistent grid: the kernel's own occupancy
 // (encode: two 4-wave groups, at most 168 VGPRs per lane and 2 x 38 KB of LDS;
-// decode: two groups, 2 x 64 KB of LDS and at most 256 VGPRs per lane),
+// decode: two groups, 2 x 80 KB of LDS and at most 256 VGPRs per lane),
 // overridable for tuning sweeps with
 // TQ_ENCODE_GROUPS_PER_CU / TQ_DECODE_GROUPS_PER_CU.
 int groups_per_cu(const char *env, int dflt)
