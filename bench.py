@@ -17,7 +17,10 @@ op re-reads data another op of the step left in the 256 MB Infinity Cache.
 Printed: one JSON line.  value = algorithmic bytes of the step / wall time per
 step (GB/s); the dominant kernel's roofline is timed with HIP events on the
 launch stream over the same timed steps; cpu_baseline times the CPU oracle on
-one full step of the same inputs.
+one full step of the same inputs.  "decode_step" (outside the timed steps, not
+part of value) times the read path at the decode-step size: 16 sequences, each a
+turbo3 K cache [8 kv heads, 32768 rows, 128] prefilled by encode, the 1-token
+append of K and V at row 32767, then q.K of 32 query heads over all rows.
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-step", action="store_true",
+                    help="skip the decode-step read-path timing")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (default: usable cores, at most 16)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,6 +175,8 @@ def main():
                 "traffic": measured_traffic(dom), "bytes_per_launch": d_bytes,
                 "avg_launch_us": round(d_us, 2)}
 
+    dstep = decode_step(tq, gen, dev, stream) if not args.no_decode_step else None
+
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -195,6 +202,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": per_op,
+        "decode_step": dstep,
     }
     print(json.dumps(out))
 
@@ -223,6 +231,57 @@ def measured_traffic(kernel: str):
     fetch = float(rec["fetch_size_kib"]) * copy_kib / float(rec["copy_fetch_size_kib"])
     write = float(rec["write_size_kib"]) * copy_kib / float(rec["copy_write_size_kib"])
     return int(round((fetch + write) * 1024))
+
+
+def decode_step(tq, gen, dev, stream, reps=20):
+    """Average times of the decode-step read path: per sequence a turbo3 K cache of
+    [8, 32768, 128] (16 sequences), rows 0..32766 prefilled by tq_encode; the 1-token
+    append of K and of V at row 32767 (two launches), and q.K of 32 query heads."""
+    import torch
+    w = gen.WORKLOADS["decode_step"]
+    B, Hkv, T_, D_, Hq = w.L, w.H, w.T, w.D, w.Hq
+    bits = 3
+    kc, kn = tq.empty_cache(bits, B, Hkv, T_, D_, dev)
+    vc, vn = tq.empty_cache(bits, B, Hkv, T_, D_, dev)
+    for b in range(B):   # prefill one sequence at a time (67 MB of fp16 each)
+        xb = gen.kv_layer(w.seed, "K", w.spec, b, Hkv, T_ - 1, D_, device=dev, T_total=T_)
+        tq.tq_encode(bits, xb.unsqueeze(0), kc[b:b + 1], kn[b:b + 1], 0)
+        del xb
+    tok = {}
+    for name in ("K", "V"):
+        t_ = torch.empty((B, Hkv, 1, D_), dtype=torch.float16, device=dev)
+        for b in range(B):
+            t_[b] = gen.kv_layer(w.seed, name, w.spec, b, Hkv, 1, D_, device=dev,
+                                 t_offset=T_ - 1, T_total=T_)
+        tok[name] = t_
+    q = gen.queries(w.seed, B, Hq, D_, device=dev)
+    scores = torch.empty((B, Hq, T_), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D_)
+    ops = [("append_kv", lambda: (tq.tq_encode(bits, tok["K"], kc, kn, T_ - 1),
+                                  tq.tq_encode(bits, tok["V"], vc, vn, T_ - 1))),
+           ("qk", lambda: tq.tq_qk_scores(bits, kc, kn, q, scale, scores))]
+    # each op back to back `reps` times between two events (the queue never drains, so
+    # host launch latency stays hidden), after two untimed launches
+    med = {}
+    for name, fn in ops:
+        fn()
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        med[name] = e0.elapsed_time(e1) * 1e3 / reps
+    qb = qk_bytes(B, Hkv, T_, 1, Hq, bits)
+    out = {"workload": f"{B} sequences x {Hkv} kv heads x {T_} rows x {D_}, {Hq} query heads, turbo3",
+           "qk_us": round(med["qk"], 2), "qk_bytes": qb,
+           "qk_GBps": round(qb / (med["qk"] * 1e-6) / 1e9, 1),
+           "qk_frac_of_hbm_peak": round(qb / (med["qk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "append_kv_us": round(med["append_kv"], 2)}
+    del kc, kn, vc, vn, scores
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
