@@ -14,13 +14,19 @@ covering both.  One step runs the whole path once:
 Each type encodes its own copy of K,V and decodes into its own buffers, so no
 op re-reads data another op of the step left in the 256 MB Infinity Cache.
 
+Before the W warm-up steps, whole steps run untimed for 0.2 s ("settle_steps"):
+the GPU raises its clocks only after tens of milliseconds of sustained load, and a
+short warm-up would time the ramp instead of the steady state.
+
 Printed: one JSON line.  value = algorithmic bytes of the step / wall time per
 step (GB/s); the dominant kernel's roofline is timed with HIP events on the
 launch stream over the same timed steps; cpu_baseline times the CPU oracle on
-one full step of the same inputs.  "decode_step" (outside the timed steps, not
-part of value) times the read path at the decode-step size: 16 sequences, each a
-turbo3 K cache [8 kv heads, 32768 rows, 128] prefilled by encode, the 1-token
-append of K and V at row 32767, then q.K of 32 query heads over all rows.
+whole steps of the same inputs (at least 10 s of CPU work).  Outside the timed
+steps and not part of value: "decode_step" times the read path at the decode-step
+size (16 sequences, each a turbo3 K cache [8 kv heads, 32768 rows, 128] prefilled
+by encode, the 1-token append of K and V at row 32767, then q.K of 32 query heads
+over all rows); "bandwidth_configs" times encode and decode of a whole 14B-shaped
+turbo3 cache and a head_dim-256 turbo2 cache.
 """
 from __future__ import annotations
 
@@ -40,6 +46,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 L, H, T, D = 1, 8, 32768, 128  # one layer
 HQ = 32                        # query heads (GQA group 4)
 COPY_CAL_BYTES = 256 << 20     # bytes read (and written) by one calibration copy
+SETTLE_S = 0.2                 # untimed steps before the warm-up (clock ramp-up)
 
 
 def codec_bytes(nblocks: int, bits: int) -> int:
@@ -59,6 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the decode-step read-path timing")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the full-cache and head_dim-256 bandwidth timings")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (default: usable cores, at most 16)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -122,6 +131,7 @@ def main():
     ops.append(("qk_turbo3", qk_bytes(1, H, T, m, HQ, 3),
                 lambda: tq.tq_qk_scores(3, kc, kn, q, scale, scores)))
     step_bytes = sum(o[1] for o in ops)
+    op_values = {f"{k}_turbo{bits}": nblk * 128 for k in ("encode", "decode") for bits in (3, 2)}
 
     def step(dom_i=-1, ev=None):
         for i, (_, _, fn) in enumerate(ops):
@@ -131,6 +141,16 @@ def main():
             if i == dom_i:
                 ev[1].record(stream)
 
+    # Settle: the GPU ramps its clocks up only after tens of milliseconds of sustained
+    # load, so whole steps run untimed for at least SETTLE_S before the W warm-up steps.
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -148,6 +168,8 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         per_op[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        if name in op_values:
+            per_op[name]["Gvalues_per_s"] = round(op_values[name] / (us * 1e-6) / 1e9, 2)
     dom = max(per_op, key=lambda k: per_op[k]["us"])   # the dominant kernel of the step
     dom_i = [o[0] for o in ops].index(dom)
     for _ in range(2):
@@ -176,6 +198,7 @@ def main():
                 "avg_launch_us": round(d_us, 2)}
 
     dstep = decode_step(tq, gen, dev, stream) if not args.no_decode_step else None
+    bw_cfgs = bandwidth_configs(tq, gen, dev, stream) if not args.no_large else None
 
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -191,7 +214,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps,
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "one_layer: K,V fp16 [8 kv_heads, 32768 tokens, 128]; turbo3+turbo2 "
@@ -203,6 +227,7 @@ def main():
         "cpu_baseline": cpu,
         "ops": per_op,
         "decode_step": dstep,
+        "bandwidth_configs": bw_cfgs,
     }
     print(json.dumps(out))
 
@@ -284,8 +309,49 @@ def decode_step(tq, gen, dev, stream, reps=20):
     return out
 
 
+def bandwidth_configs(tq, gen, dev, stream, reps=10):
+    """Encode then decode of two whole caches, the sizes where launch ramp and tail
+    stop mattering: a 14B-shaped turbo3 cache (48 layers x 8 kv heads x 32768 x 128,
+    K and V as one [96, 8, 32768, 128] tensor, 6.4 GB of fp16) and a head_dim-256
+    turbo2 cache (32 layers x 4 kv heads x 32768 x 256, K and V, 4.3 GB).  Average of
+    `reps` back-to-back launches per op after ten untimed ones."""
+    import torch
+    out = {}
+    for wname, bits in (("full_cache_14b", 3), ("head_dim_256", 2)):
+        w = gen.WORKLOADS[wname]
+        Lx = 2 * w.L
+        x = torch.empty((Lx, w.H, w.T, w.D), dtype=torch.float16, device=dev)
+        for i, name in enumerate(("K", "V")):
+            for l in range(w.L):
+                x[i * w.L + l] = gen.kv_layer(w.seed, name, w.spec, l, w.H, w.T, w.D, device=dev)
+        codes, norms = tq.empty_cache(bits, Lx, w.H, w.T, w.D, dev)
+        y = torch.empty_like(x)
+        nblk = x.numel() // 128
+        res = {"workload": f"{w.L} layers x {w.H} kv heads x {w.T} x {w.D}, K and V, turbo{bits}"}
+        for op, fn in (("encode", lambda: tq.tq_encode(bits, x, codes, norms, 0)),
+                       ("decode", lambda: tq.tq_decode(bits, codes, norms, 0, y))):
+            for _ in range(10):   # about 15 ms of load: clocks at their sustained level
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            nb = codec_bytes(nblk, bits)
+            res[op] = {"us": round(us, 1), "bytes": nb, "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "Gvalues_per_s": round(nblk * 128 / (us * 1e-6) / 1e9, 1)}
+        out[wname] = res
+        del x, y, codes, norms
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
-    """The CPU oracle, untuned, on one full step of the same inputs (host copies)."""
+    """The CPU oracle, untuned, on whole steps of the same inputs (host copies),
+    repeated until at least 10 s of CPU work."""
     import numpy as np
 
     import oracle
@@ -295,22 +361,33 @@ def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
     qn = q.cpu().numpy()
     tk = tok.cpu().numpy()
     m = D // 128
+    def one_step():
+        caches = {}
+        for bits in (3, 2):
+            c = np.zeros((2, H, T, m, 16 * bits), np.uint8)
+            n = np.zeros((2, H, T, m), np.float16)
+            oracle.encode(bits, x, c, n, nthreads=threads)
+            caches[bits] = (c, n)
+        for bits in (3, 2):
+            oracle.decode(bits, *caches[bits], 0, T, nthreads=threads)
+        oracle.encode(3, tk, *caches[3], t0=T - 1, nthreads=threads)
+        c3, n3 = caches[3]
+        oracle.qk_scores(3, c3[0:1], n3[0:1], qn, scale, nthreads=threads)
+
+    # whole steps until at least min_seconds of CPU work (a bounded sample)
+    min_seconds = 10.0
     t0 = time.perf_counter()
-    caches = {}
-    for bits in (3, 2):
-        c = np.zeros((2, H, T, m, 16 * bits), np.uint8)
-        n = np.zeros((2, H, T, m), np.float16)
-        oracle.encode(bits, x, c, n, nthreads=threads)
-        caches[bits] = (c, n)
-    for bits in (3, 2):
-        oracle.decode(bits, *caches[bits], 0, T, nthreads=threads)
-    oracle.encode(3, tk, *caches[3], t0=T - 1, nthreads=threads)
-    c3, n3 = caches[3]
-    oracle.qk_scores(3, c3[0:1], n3[0:1], qn, scale, nthreads=threads)
-    el = time.perf_counter() - t0
-    return {"value": round(step_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+    steps = 0
+    while True:
+        one_step()
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": round(step_bytes * steps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(el, 2),
-            "sample": "one full step of the same workload on host copies of the same inputs"}
+            "sample": f"{steps} full steps of the same workload (one layer, K and V) on host "
+                      f"copies of the same inputs, repeated until at least {min_seconds:.0f} s"}
 
 
 if __name__ == "__main__":
