@@ -125,6 +125,18 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b)
 __device__ __forceinline__ void set_f32_round_down() { __builtin_amdgcn_s_setreg(0x801, 2); }
 __device__ __forceinline__ void set_f32_round_nearest() { __builtin_amdgcn_s_setreg(0x801, 0); }
 
+// The codebook levels into LDS.  Indexing the kernel-argument copy with a per-lane
+// index would turn every table entry into a round trip to memory; one lane copies
+// the levels with constant indices (scalar loads) and the caller barriers.
+__device__ __forceinline__ void levels_to_lds(float *lv, const Codebook &cb)
+{
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            lv[k] = cb.levels[k];
+    }
+}
+
 // Order LDS traffic between the lanes of one wavefront (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -504,9 +516,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
     constexpr int kTableBytes = NE * kLdsCopies8 * 8;
     // one LDS buffer, the table first
     __shared__ __attribute__((aligned(16))) uint8_t smem[kTableBytes + kWavesPerGroup * kTileBytes];
+    // the levels pass through the first tile's bytes, which no wave uses before the
+    // barrier that ends the table build (two 80 KB groups fill a CU's 160 KB exactly)
+    float *lv = (float *)(smem + kTableBytes);
+    levels_to_lds(lv, cb);
+    __syncthreads();
     for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += blockDim.x) {
         const uint32_t e = i / kLdsCopies8;
-        const float y0 = cb.levels[e & ((1u << BITS) - 1u)], y1 = cb.levels[e >> BITS];
+        const float y0 = lv[e & ((1u << BITS) - 1u)], y1 = lv[e >> BITS];
         *(float2 *)(smem + i * 8) = float2{y0 + y1, y0 - y1};
     }
     __syncthreads();
@@ -741,18 +758,21 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 
     // lookup table of (yh, yl) pairs in the B order above: entry e holds the values
     // of codes e & 7, e >> 3 (turbo3) or (e >> 2 k) & 3, k = 0..3 (turbo2)
+    __shared__ float lv[8];
+    levels_to_lds(lv, cb);
+    __syncthreads();
     for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * NC); i += blockDim.x) {
         const uint32_t e = i / NC;
         if constexpr (BITS == 3) {
             _Float16 a0, a1, c0, c1;
-            split_f16(cb.levels[e & 7], a0, c0);
-            split_f16(cb.levels[e >> 3], a1, c1);
+            split_f16(lv[e & 7], a0, c0);
+            split_f16(lv[e >> 3], a1, c1);
             *(uint2 *)(table + i * EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         } else {
             _Float16 a[4], c[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                split_f16(cb.levels[(e >> (2 * k)) & 3], a[k], c[k]);
+                split_f16(lv[(e >> (2 * k)) & 3], a[k], c[k]);
             *(uint4 *)(table + i * EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
                                                 pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
         }
