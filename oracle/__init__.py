@@ -66,6 +66,9 @@ def _load():
     lib.tqo_decode.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i32]
     lib.tqo_qk.restype = i32
     lib.tqo_qk.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl, vp, i32]
+    lib.tqo_attn_decode.restype = i32
+    lib.tqo_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl,
+                                    vp, i32]
     _lib = lib
     return lib
 
@@ -217,3 +220,26 @@ def qk_scores(bits: int, k_codes, k_norms, q, scale: float, T: int | None = None
     if rc:
         raise ValueError("tqo_qk failed")
     return scores
+
+
+def attn_decode(bits: int, k_codes, k_norms, v_codes, v_norms, q, scale: float,
+                T: int | None = None, nthreads: int | None = None):
+    """K and V caches [B,Hkv,Tc,D/128,...] + q fp16 [B,Hq,D] → out f64 [B,Hq,D]:
+    softmax over rows [0, T) of scale * q.k_hat, applied to v_hat."""
+    _check_bits(bits)
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    k_norms, v_norms, q = _c16(k_norms), _c16(v_norms), _c16(q)
+    B, Hkv, Tc, m, cb = k_codes.shape
+    Bq, Hq, D = q.shape
+    if (cb != code_bytes(bits) or v_codes.shape != k_codes.shape or k_norms.shape != (B, Hkv, Tc, m)
+            or v_norms.shape != k_norms.shape or Bq != B or D != m * BLOCK):
+        raise ValueError("bad q / cache arrays")
+    T = Tc if T is None else T
+    out = np.zeros((B, Hq, D), np.float64)
+    rc = _load().tqo_attn_decode(bits, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+                                 B, Hkv, Tc, D, T, _ptr(q), Hq, float(scale), _ptr(out),
+                                 nthreads or default_threads())
+    if rc:
+        raise ValueError("tqo_attn_decode failed")
+    return out

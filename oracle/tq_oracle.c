@@ -558,3 +558,105 @@ int tqo_qk(int bits, const uint8_t *k_codes, const uint16_t *k_norms, int64_t B,
     parallel_for(B * Hkv, nthreads, qk_range, &c);
     return 0;
 }
+
+/* Decode attention of one query token per (sequence, query head) over the
+ * compressed K and V caches: out[b,h,:] = sum_t p_t * v_hat[b,h/G,t,:] with
+ * p = softmax_t(scale * q[b,h,:] . k_hat[b,h/G,t,:]) over cache rows t in
+ * [0, T).  The article's closing section ("現在の実装と、これから") names this
+ * fusion -- attention read straight from the compressed cache -- as the next
+ * step; the arithmetic is the plain definition of scaled dot-product attention
+ * with grouped-query heads: max-subtracted exponentials, their sum, the weighted
+ * sum of the dequantised values, all in binary64 and from the unrounded decodes.
+ * One work item = one (b, kv head) pair. */
+typedef struct {
+    codebook_t cb;
+    const uint8_t *kc, *vc;
+    const uint16_t *kn, *vn;
+    int64_t B, Hkv, Tc, D, T, Hq;
+    const uint16_t *q;
+    double scale;
+    double *out;
+} attn_ctx;
+
+static void attn_range(void *p, int64_t lo, int64_t hi)
+{
+    attn_ctx *c = (attn_ctx *)p;
+    int64_t m = c->D / TQO_BLOCK, G = c->Hq / c->Hkv;
+    int cbytes = 16 * c->cb.bits;
+    double *row = (double *)malloc(sizeof(double) * (size_t)c->D);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)(c->D * G));
+    double *s = (double *)malloc(sizeof(double) * (size_t)(c->T * G));
+    for (int64_t bg = lo; bg < hi; ++bg) {
+        int64_t b = bg / c->Hkv, g = bg % c->Hkv;
+        for (int64_t r = 0; r < G; ++r)
+            for (int64_t d = 0; d < c->D; ++d)
+                qd[r * c->D + d] = tqo_half_to_double(c->q[(b * c->Hq + g * G + r) * c->D + d]);
+        /* logits */
+        for (int64_t t = 0; t < c->T; ++t) {
+            for (int64_t j = 0; j < m; ++j) {
+                int64_t blk = (bg * c->Tc + t) * m + j;
+                decode_block(&c->cb, c->kc + blk * cbytes, c->kn[blk], row + j * TQO_BLOCK);
+            }
+            for (int64_t r = 0; r < G; ++r) {
+                double acc = 0.0;
+                for (int64_t d = 0; d < c->D; ++d)
+                    acc += qd[r * c->D + d] * row[d];
+                s[r * c->T + t] = c->scale * acc;
+            }
+        }
+        /* softmax weights: exp(s - max) / sum */
+        for (int64_t r = 0; r < G; ++r) {
+            double mx = s[r * c->T];
+            for (int64_t t = 1; t < c->T; ++t)
+                if (s[r * c->T + t] > mx)
+                    mx = s[r * c->T + t];
+            double sum = 0.0;
+            for (int64_t t = 0; t < c->T; ++t) {
+                s[r * c->T + t] = exp(s[r * c->T + t] - mx);
+                sum += s[r * c->T + t];
+            }
+            for (int64_t t = 0; t < c->T; ++t)
+                s[r * c->T + t] /= sum;
+        }
+        /* weighted sum of the dequantised values */
+        for (int64_t r = 0; r < G; ++r)
+            for (int64_t d = 0; d < c->D; ++d)
+                c->out[(b * c->Hq + g * G + r) * c->D + d] = 0.0;
+        for (int64_t t = 0; t < c->T; ++t) {
+            for (int64_t j = 0; j < m; ++j) {
+                int64_t blk = (bg * c->Tc + t) * m + j;
+                decode_block(&c->cb, c->vc + blk * cbytes, c->vn[blk], row + j * TQO_BLOCK);
+            }
+            for (int64_t r = 0; r < G; ++r) {
+                double w = s[r * c->T + t];
+                double *o = c->out + (b * c->Hq + g * G + r) * c->D;
+                for (int64_t d = 0; d < c->D; ++d)
+                    o[d] += w * row[d];
+            }
+        }
+    }
+    free(row);
+    free(qd);
+    free(s);
+}
+
+int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
+                    const uint8_t *v_codes, const uint16_t *v_norms, int64_t B, int64_t Hkv,
+                    int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
+                    double *out, int nthreads)
+{
+    attn_ctx c;
+    if (get_codebook(bits, &c.cb) || D <= 0 || D % TQO_BLOCK || B < 0 || Hkv <= 0 || Hq <= 0 ||
+        Hq % Hkv || T < 1 || T > Tc)
+        return -1;
+    c.kc = k_codes;
+    c.kn = k_norms;
+    c.vc = v_codes;
+    c.vn = v_norms;
+    c.B = B; c.Hkv = Hkv; c.Tc = Tc; c.D = D; c.T = T; c.Hq = Hq;
+    c.q = q;
+    c.scale = scale;
+    c.out = out;
+    parallel_for(B * Hkv, nthreads, attn_range, &c);
+    return 0;
+}

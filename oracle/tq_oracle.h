@@ -54,6 +54,14 @@ int tqo_qk(int bits, const uint8_t *k_codes, const uint16_t *k_norms, int64_t B,
            int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
            double *scores, int nthreads);
 
+/* Decode attention: K and V caches [B,Hkv,Tc,D/128] packed, q fp16 [B,Hq,D],
+ * out [B,Hq,D] (double) = softmax over rows [0, T) of scale * q.k_hat, applied
+ * to v_hat.  T >= 1. */
+int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
+                    const uint8_t *v_codes, const uint16_t *v_norms, int64_t B, int64_t Hkv,
+                    int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
+                    double *out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

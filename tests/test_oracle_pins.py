@@ -403,3 +403,84 @@ def test_qk_against_dense_dot(bits):
     ref = np.einsum("bgrd,bgtd->bgrt", q.astype(np.float64).reshape(B, Hkv, G, D), khat)
     ref = scale * ref.reshape(B, Hkv * G, T)
     np.testing.assert_allclose(s, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- decode attention
+
+def _attn_inputs(bits, seed, B, Hkv, Tc, D, G):
+    rng = np.random.default_rng(seed)
+    m = D // 128
+    caches = []
+    for _ in range(2):   # K, V
+        x = (rng.standard_normal((B, Hkv, Tc, D)) * np.exp(rng.uniform(-1, 1, (B, Hkv, Tc, 1))))
+        codes = np.zeros((B, Hkv, Tc, m, 16 * bits), np.uint8)
+        norms = np.zeros((B, Hkv, Tc, m), np.float16)
+        oracle.encode(bits, x.astype(np.float16), codes, norms)
+        caches.append((codes, norms))
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float16)
+    return caches, q
+
+
+def _dense_hat(bits, codes, norms):
+    """Decoded cache rebuilt here: numpy unpacking, codebook lookup, dense H."""
+    B, Hkv, Tc, m, _ = codes.shape
+    lv, _, _ = oracle.codebook(bits)
+    y = lv[_unpack(codes, bits)].reshape(B, Hkv, Tc, m, 128)
+    return ((y @ H128.T) * (norms.astype(np.float64)[..., None] / 128)).reshape(B, Hkv, Tc, m * 128)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_attn_decode_against_dense_softmax(bits):
+    """out = softmax(scale q . k_hat) v_hat with grouped heads, against scipy's softmax
+    over keys and values rebuilt densely from the packed caches."""
+    import scipy.special
+    B, Hkv, G, Tc, T, D = 2, 2, 3, 11, 9, 256
+    (kc, kn), (vc, vn) = _attn_inputs(bits, 21, B, Hkv, Tc, D, G)[0]
+    q = _attn_inputs(bits, 21, B, Hkv, Tc, D, G)[1]
+    scale = 1 / math.sqrt(D)
+    out = oracle.attn_decode(bits, kc, kn, vc, vn, q, scale, T=T)
+    kh = _dense_hat(bits, kc, kn)[:, :, :T]
+    vh = _dense_hat(bits, vc, vn)[:, :, :T]
+    qd = q.astype(np.float64).reshape(B, Hkv, G, D)
+    s = scale * np.einsum("bgrd,bgtd->bgrt", qd, kh)
+    p = scipy.special.softmax(s, axis=-1)
+    ref = np.einsum("bgrt,bgtd->bgrd", p, vh).reshape(B, Hkv * G, D)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_attn_decode_special_cases(bits):
+    """T = 1: the weight is exactly 1, out = v_hat of row 0.  q = 0: equal weights,
+    out = the mean of v_hat over the rows.  A huge scale: the weights become one-hot
+    on the highest-scoring row (exp underflows to 0 for the others)."""
+    B, Hkv, G, Tc, D = 1, 2, 2, 8, 128
+    (kc, kn), (vc, vn) = _attn_inputs(bits, 22, B, Hkv, Tc, D, G)[0]
+    q = _attn_inputs(bits, 22, B, Hkv, Tc, D, G)[1]
+    vh = _dense_hat(bits, vc, vn)
+    out1 = oracle.attn_decode(bits, kc, kn, vc, vn, q, 0.3, T=1)
+    np.testing.assert_allclose(out1, np.repeat(vh[:, :, 0], G, axis=1), rtol=1e-13, atol=1e-14)
+    out0 = oracle.attn_decode(bits, kc, kn, vc, vn, np.zeros_like(q), 0.3, T=Tc)
+    np.testing.assert_allclose(out0, np.repeat(vh.mean(axis=2), G, axis=1), rtol=1e-12,
+                               atol=1e-13 * np.abs(vh).max())
+    big = 1e6
+    outb = oracle.attn_decode(bits, kc, kn, vc, vn, q, big, T=Tc)
+    s = oracle.qk_scores(bits, kc, kn, q, 1.0, T=Tc)          # [B, Hq, T]
+    top = s.argmax(axis=-1)
+    srt = np.sort(s, axis=-1)
+    assert np.all((srt[..., -1] - srt[..., -2]) * big > 800)     # exp(-800) == 0 in binary64
+    vdec, _ = oracle.decode(bits, vc, vn, 0, Tc)                 # the oracle's own decode
+    for h in range(Hkv * G):
+        np.testing.assert_array_equal(outb[0, h], vdec[0, h // G, top[0, h]])
+        np.testing.assert_allclose(outb[0, h], vh[0, h // G, top[0, h]], rtol=1e-13, atol=1e-14)
+
+
+def test_attn_decode_grouping_equals_repeated_heads():
+    """Grouped-query attention equals ordinary multi-head attention over K and V caches
+    repeated G times along the head axis (the GQA mapping kv head = h // G)."""
+    bits, B, Hkv, G, Tc, D = 3, 2, 2, 4, 10, 128
+    (kc, kn), (vc, vn) = _attn_inputs(bits, 23, B, Hkv, Tc, D, G)[0]
+    q = _attn_inputs(bits, 23, B, Hkv, Tc, D, G)[1]
+    a = oracle.attn_decode(bits, kc, kn, vc, vn, q, 0.2, T=Tc)
+    rep = lambda z: np.repeat(z, G, axis=1)
+    b = oracle.attn_decode(bits, rep(kc), rep(kn), rep(vc), rep(vn), q, 0.2, T=Tc)
+    np.testing.assert_array_equal(a, b)
