@@ -64,7 +64,8 @@ enum tq_status {
     TQ_ERR_NULL = -4,   /* NULL pointer where there is work to do */
     TQ_ERR_ALIGN = -5,  /* x / q / codes not 16-byte, norms not 2-byte, scores not 4-byte aligned */
     TQ_ERR_ALIAS = -6,  /* an output range overlaps an input range or another output */
-    TQ_ERR_DEVICE = -7  /* HIP reported an error for the launch */
+    TQ_ERR_DEVICE = -7,      /* HIP reported an error for the launch */
+    TQ_ERR_WORKSPACE = -8    /* workspace smaller than tq_attn_workspace_bytes */
 };
 
 /* Largest head_dim tq_qk_scores accepts (16 blocks per vector). */
@@ -117,6 +118,30 @@ int tq_decode(int type, const void *codes, const void *norms, int64_t L, int64_t
 int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
                  int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq, float scale,
                  float *scores, void *stream);
+
+/* Bytes of device workspace tq_attn_decode needs for these sizes (0 when B == 0);
+ * a negative tq_status for sizes tq_attn_decode would reject.  Depends on the sizes
+ * only, not on the device. */
+int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, int64_t D,
+                                int64_t T, int64_t Hq);
+
+/* Decode attention straight from the compressed caches: the fused read of section
+ * "現在の実装と、これから" carried through softmax and the values, one query
+ * token per (sequence, query head):
+ *   k_codes, k_norms, v_codes, v_norms  device K and V caches [B, Hkv, Tc, D] (read only)
+ *   q          device fp16 [B, Hq, D], 16-byte aligned (read only)
+ *   out        device fp32 [B, Hq, D], 4-byte aligned
+ *   workspace  device, at least tq_attn_workspace_bytes(...) bytes, 16-byte aligned;
+ *              scratch for per-chunk partial results, overwritten, no initial
+ *              contents needed; calls that share a workspace must not overlap
+ * out[b, h, :] = sum_t p_t v_hat[b, h/G, t, :] with p = softmax over rows t in [0, T)
+ * of scale * q[b, h, :] . k_hat[b, h/G, t, :], G = Hq / Hkv, k_hat and v_hat the
+ * decoded keys and values kept in float.  Requires D == 128, T >= 1 (when B > 0),
+ * T <= Tc, Hq % Hkv == 0.  Two kernel launches on `stream`. */
+int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
+                   const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                   const void *q, int64_t Hq, float scale, float *out, void *workspace,
+                   int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

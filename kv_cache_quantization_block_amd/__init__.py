@@ -34,7 +34,8 @@ lib_path = os.path.join(_PKG, "libtq.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "tq.h")
 
 STATUS = {0: "TQ_OK", -1: "TQ_ERR_TYPE", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_RANGE",
-          -4: "TQ_ERR_NULL", -5: "TQ_ERR_ALIGN", -6: "TQ_ERR_ALIAS", -7: "TQ_ERR_DEVICE"}
+          -4: "TQ_ERR_NULL", -5: "TQ_ERR_ALIGN", -6: "TQ_ERR_ALIAS", -7: "TQ_ERR_DEVICE",
+          -8: "TQ_ERR_WORKSPACE"}
 
 
 class TQError(RuntimeError):
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
     L.tq_decode.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp]
     L.tq_qk_scores.restype = i32
     L.tq_qk_scores.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp, vp]
+    L.tq_attn_workspace_bytes.restype = i64
+    L.tq_attn_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
+    L.tq_attn_decode.restype = i32
+    L.tq_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp,
+                                 vp, i64, vp]
     _lib = L
     return L
 
@@ -197,3 +203,43 @@ def tq_qk_scores(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, q: tor
                             _dev(scores, "scores", torch.float32), _stream(stream))
     if rc:
         raise TQError(rc, "tq_qk_scores")
+
+
+def tq_attn_workspace_bytes(type: int, B: int, Hkv: int, Tc: int, D: int, T: int, Hq: int) -> int:
+    """Device workspace bytes tq_attn_decode needs for these sizes."""
+    r = lib().tq_attn_workspace_bytes(type, B, Hkv, Tc, D, T, Hq)
+    if r < 0:
+        raise TQError(int(r), "tq_attn_workspace_bytes")
+    return int(r)
+
+
+def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor,
+                   v_norms: torch.Tensor, q: torch.Tensor, scale: float, out: torch.Tensor,
+                   T: int | None = None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    """out [B, Hq, D] (fp32) = softmax over rows [0, T) of scale * q . k_hat, applied to v_hat
+    (asynchronous).  workspace: a uint8 device tensor of at least tq_attn_workspace_bytes;
+    when None, one is allocated here with torch (the library itself never allocates)."""
+    B, Hkv, Tc, D = _cache_dims(k_codes, k_norms, type)
+    if _cache_dims(v_codes, v_norms, type) != (B, Hkv, Tc, D):
+        raise ValueError("K and V caches must have the same shape")
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, Hq, D] matching the cache")
+    Hq = q.shape[1]
+    if out.dim() != 3 or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    T = Tc if T is None else int(T)
+    need = tq_attn_workspace_bytes(type, B, Hkv, Tc, D, T, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-d uint8 tensor")
+    rc = lib().tq_attn_decode(type, _dev(k_codes, "k_codes", torch.uint8),
+                              _dev(k_norms, "k_norms", torch.float16),
+                              _dev(v_codes, "v_codes", torch.uint8),
+                              _dev(v_norms, "v_norms", torch.float16), B, Hkv, Tc, D, T,
+                              _dev(q, "q", torch.float16), Hq, float(scale),
+                              _dev(out, "out", torch.float32),
+                              _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                              _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_attn_decode")

@@ -95,6 +95,7 @@ const char *tq_status_string(int status)
     case TQ_ERR_ALIGN: return "TQ_ERR_ALIGN: misaligned pointer";
     case TQ_ERR_ALIAS: return "TQ_ERR_ALIAS: output overlaps another buffer";
     case TQ_ERR_DEVICE: return "TQ_ERR_DEVICE: HIP launch failed";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE: workspace smaller than tq_attn_workspace_bytes";
     default: return "unknown tq_status";
     }
 }
@@ -189,3 +190,67 @@ int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, 
 }
 
 }  // extern "C"
+
+// Shapes of the decode attention call (D = 128); fills the cache blocks of one cache.
+static int check_attn_shape(int type, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                            int64_t Hq, int64_t *cache_blocks)
+{
+    if (!valid_type(type))
+        return TQ_ERR_TYPE;
+    if (B < 0 || Hkv <= 0 || Hq <= 0 || Tc < 0 || T < 0 || D != tq::kBlock || Hq % Hkv ||
+        (B > 0 && T < 1))
+        return TQ_ERR_SHAPE;
+    if (T > Tc)
+        return TQ_ERR_RANGE;
+    int64_t nq;
+    if (!mul4(B, Hkv, Tc, 1, cache_blocks) || *cache_blocks > ((int64_t)1 << 40) ||
+        !mul4(B, Hq, D, 1, &nq) || T > 65535LL * 1024 || B * Hq > INT32_MAX / 4)
+        return TQ_ERR_SHAPE;
+    return TQ_OK;
+}
+
+int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, int64_t D,
+                                int64_t T, int64_t Hq)
+{
+    int64_t cache_blocks;
+    const int st = check_attn_shape(type, B, Hkv, Tc, D, T, Hq, &cache_blocks);
+    if (st != TQ_OK)
+        return st;
+    if (B == 0)
+        return 0;
+    return tq::attn_workspace_bytes(B, Hkv, T, Hq);
+}
+
+int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
+                   const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                   const void *q, int64_t Hq, float scale, float *out, void *workspace,
+                   int64_t workspace_bytes, void *stream)
+{
+    int64_t cache_blocks;
+    const int st = check_attn_shape(type, B, Hkv, Tc, D, T, Hq, &cache_blocks);
+    if (st != TQ_OK)
+        return st;
+    if (B == 0)
+        return TQ_OK;
+    if (!k_codes || !k_norms || !v_codes || !v_norms || !q || !out || !workspace)
+        return TQ_ERR_NULL;
+    if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q, 16) ||
+        !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(out, 4) ||
+        !aligned(workspace, 16))
+        return TQ_ERR_ALIGN;
+    const int64_t need = tq::attn_workspace_bytes(B, Hkv, T, Hq);
+    if (workspace_bytes < need)
+        return TQ_ERR_WORKSPACE;
+    const int64_t ob = B * Hq * D * 4, cb = cache_blocks * 16 * type, nb = cache_blocks * 2;
+    const void *ins[5] = {k_codes, k_norms, v_codes, v_norms, q};
+    const int64_t inb[5] = {cb, nb, cb, nb, B * Hq * D * 2};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(out, ob, ins[i], inb[i]) || overlap(workspace, need, ins[i], inb[i]))
+            return TQ_ERR_ALIAS;
+    if (overlap(out, ob, workspace, need))
+        return TQ_ERR_ALIAS;
+    return tq::launch_attn(type, k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc, T, q, Hq, scale,
+                           out, workspace, stream)
+               ? TQ_ERR_DEVICE
+               : TQ_OK;
+}

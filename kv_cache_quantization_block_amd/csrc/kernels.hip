@@ -667,6 +667,147 @@ __device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
     lo = (_Float16)(x - (float)hi);
 }
 
+
+// The q.K table (two-value entries for turbo3, four-value for turbo2): entry e,
+// copy c at (e * NC + c) * EB; lane l reads copy l % NC.
+template <int BITS>
+struct QkTable {
+    static constexpr int NE = BITS == 3 ? 64 : 256;           // entries (two / four codes)
+    static constexpr int EB = BITS == 3 ? 8 : 16;             // bytes per entry
+    static constexpr int NC = BITS == 3 ? kLdsCopies8 : 8;    // copies
+    static constexpr int ES = BITS == 3 ? 8 : 7;              // log2 of the entry stride NC * EB
+    static_assert(NC * EB == (1 << ES), "entry stride");
+    static_assert(NE * NC * EB == qk_table_bytes(BITS), "table size");
+};
+
+// Fills the table of (yh, yl) pairs in the B order: entry e holds the values of codes
+// e & 7, e >> 3 (turbo3) or (e >> 2 k) & 3, k = 0..3 (turbo2).  Whole workgroup; lv
+// are the levels, already in LDS.
+template <int BITS>
+__device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv)
+{
+    using Tb = QkTable<BITS>;
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(Tb::NE * Tb::NC); i += blockDim.x) {
+        const uint32_t e = i / Tb::NC;
+        if constexpr (BITS == 3) {
+            _Float16 a0, a1, c0, c1;
+            split_f16(lv[e & 7], a0, c0);
+            split_f16(lv[e >> 3], a1, c1);
+            *(uint2 *)(table + i * Tb::EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
+        } else {
+            _Float16 a[4], c[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                split_f16(lv[(e >> (2 * k)) & 3], a[k], c[k]);
+            *(uint4 *)(table + i * Tb::EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
+                                                    pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
+        }
+    }
+}
+
+// Query operands.  Wave w prepares heads w and w + 4 of the pass (h0 .. h0 + nh - 1):
+// rotates every 128-slice (lane l holds positions l and 64 + l; span 64 in-lane, spans
+// 32..1 across lanes), takes the head's largest |q'|, then writes x = q' * scale / 128 *
+// 2^(14 - e) as hi (row hh) and lo (row 8 + hh) of qa [m][16][128], and 2^(e - 14) to
+// pw_s[hh].  Heads past nh get zero rows.  The caller barriers afterwards.
+template <bool ONE_BLOCK>
+__device__ __forceinline__ void qk_prepare_queries(_Float16 *qa, float *pw_s,
+                                                   const uint16_t *__restrict__ q, uint32_t b,
+                                                   uint32_t Hq, uint32_t h0, uint32_t nh,
+                                                   uint32_t m, uint32_t wave, uint32_t lane,
+                                                   float scale)
+{
+    auto rotate = [&](const uint16_t *v, float &a, float &c) {
+        a = (float)__builtin_bit_cast(_Float16, v[lane]);
+        c = (float)__builtin_bit_cast(_Float16, v[64 + lane]);
+        const float s0 = a + c;
+        c = a - c;
+        a = s0;
+#pragma unroll
+        for (int h = 32; h >= 1; h >>= 1) {
+            const float pa = __shfl_xor(a, h, 64), pc = __shfl_xor(c, h, 64);
+            const bool up = (lane & (uint32_t)h) != 0u;
+            a = up ? pa - a : a + pa;
+            c = up ? pc - c : c + pc;
+        }
+    };
+    for (uint32_t hh = wave; hh < (uint32_t)kQkHeads; hh += kWavesPerGroup) {
+        _Float16 *hi_row = qa + hh * kBlock, *lo_row = qa + (kQkHeads + hh) * kBlock;
+        if (hh < nh) {
+            const uint16_t *qv = q + ((size_t)b * Hq + h0 + hh) * ((size_t)m * kBlock);
+            float mx = 0.0f, a1 = 0.0f, c1 = 0.0f;   // a1, c1: the single slice when m == 1
+            for (uint32_t j = 0; j < m; ++j) {
+                float a, c;
+                rotate(qv + j * kBlock, a, c);
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(c)));
+                a1 = a;
+                c1 = c;
+            }
+#pragma unroll
+            for (int h = 32; h >= 1; h >>= 1)
+                mx = __builtin_fmaxf(mx, __shfl_xor(mx, h, 64));
+            int e = 0;
+            (void)frexpf(mx * __builtin_fabsf(scale) * (1.0f / 128.0f), &e);
+            const float f = ldexpf(scale * (1.0f / 128.0f), 14 - e);
+            for (uint32_t j = 0; j < m; ++j) {
+                float a = a1, c = c1;
+                if (!ONE_BLOCK)
+                    rotate(qv + j * kBlock, a, c);
+                _Float16 ah, al, ch, cl;
+                split_f16(a * f, ah, al);
+                split_f16(c * f, ch, cl);
+                hi_row[j * 2048 + lane] = ah;
+                hi_row[j * 2048 + 64 + lane] = ch;
+                lo_row[j * 2048 + lane] = al;
+                lo_row[j * 2048 + 64 + lane] = cl;
+            }
+            if (lane == 0)
+                pw_s[hh] = ldexpf(1.0f, e - 14);
+        } else {
+            for (uint32_t j = 0; j < m; ++j) {
+                hi_row[j * 2048 + lane] = hi_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
+                lo_row[j * 2048 + lane] = lo_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
+            }
+            if (lane == 0)
+                pw_s[hh] = 0.0f;
+        }
+    }
+}
+
+// One 16-row unit of q.K: the eight 16 x 16 x 32 products of the query operands A
+// (row lane % 16, values of the lane's run) with the lane's 32 key codes w (row
+// lane % 16, run lane / 16), looked up in this lane's table copy tcopy.  Result rows
+// 4 (lane / 16) .. + 3 of column lane % 16, not yet scaled by the norm.
+template <int BITS>
+__device__ __forceinline__ f4_t qk_unit(const h8_t (&A)[8], const uint32_t *w, uint32_t tcopy)
+{
+    constexpr int ES = QkTable<BITS>::ES;
+    // two accumulation chains (even / odd chunks) halve the dependent MFMA latency
+    f4_t D[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        u4_t bv;
+        if constexpr (BITS == 3) {
+            uint32_t o[2];   // LDS addresses of the entries of v0 v1 and v2 v3
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int bit = 12 * c + 6 * k2, wi = bit >> 5, sh = bit & 31;
+                const uint32_t e = sh <= 26 ? __builtin_amdgcn_ubfe(w[wi], sh, 6)
+                                            : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
+                o[k2] = lshl_add<ES>(e, tcopy);   // e * NC * EB + copy
+            }
+            const uint64_t r0 = lds_load<uint64_t>(o[0]), r1 = lds_load<uint64_t>(o[1]);
+            bv = u4_t{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)};
+        } else {
+            const uint32_t e = __builtin_amdgcn_ubfe(w[c >> 2], 8 * (c & 3), 8);
+            bv = lds_load<u4_t>(lshl_add<ES>(e, tcopy));
+        }
+        D[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], __builtin_bit_cast(h8_t, bv),
+                                                          D[c & 1], 0, 0, 0);
+    }
+    return D[0] + D[1];
+}
+
 // BITS: 2 or 3.  ONE_BLOCK: D == 128 (the query operands stay in registers).  A
 // workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head)
 // for up to eight query heads (pass blockIdx.x % passes).
@@ -680,15 +821,10 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                                                     uint32_t tpg, float scale, Codebook cb)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t qk_smem[];
-    constexpr int NE = BITS == 3 ? 64 : 256;   // table entries (two / four codes)
-    constexpr int EB = BITS == 3 ? 8 : 16;     // bytes per entry
-    constexpr int NC = BITS == 3 ? kLdsCopies8 : 8;   // copies
-    constexpr int ES = BITS == 3 ? 8 : 7;      // log2 of the entry stride NC * EB
+    constexpr int NC = QkTable<BITS>::NC;
+    constexpr int EB = QkTable<BITS>::EB;
     constexpr int CB = 16 * BITS;              // code bytes per block
     constexpr int LW = BITS;                   // code words per lane (32 codes)
-    static_assert(NC * EB == (1 << ES), "entry stride");
-    static_assert(NE * NC * EB == qk_table_bytes(BITS), "table size");
-    // Copy c of entry e sits at (e * NC + c) * EB and lane l reads copy l % NC.
     uint8_t *table = qk_smem;
     _Float16 *qa = (_Float16 *)(qk_smem + qk_table_bytes(BITS));   // [m][16][128]
     float *pw_s = (float *)(qk_smem + qk_table_bytes(BITS) + (size_t)m * 16 * kBlock * 2);
@@ -756,87 +892,12 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     if constexpr (ONE_BLOCK)
         fetch_norms(0, nna, nnb);
 
-    // lookup table of (yh, yl) pairs in the B order above: entry e holds the values
-    // of codes e & 7, e >> 3 (turbo3) or (e >> 2 k) & 3, k = 0..3 (turbo2)
     __shared__ float lv[8];
     levels_to_lds(lv, cb);
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * NC); i += blockDim.x) {
-        const uint32_t e = i / NC;
-        if constexpr (BITS == 3) {
-            _Float16 a0, a1, c0, c1;
-            split_f16(lv[e & 7], a0, c0);
-            split_f16(lv[e >> 3], a1, c1);
-            *(uint2 *)(table + i * EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
-        } else {
-            _Float16 a[4], c[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                split_f16(lv[(e >> (2 * k)) & 3], a[k], c[k]);
-            *(uint4 *)(table + i * EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
-                                                pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
-        }
-    }
+    qk_fill_table<BITS>(table, lv);
 
-    // Query operands.  Wave w prepares heads w and w + 4: rotates every 128-slice
-    // (lane l holds positions l and 64 + l; span 64 in-lane, spans 32..1 across
-    // lanes), takes the head's largest |q'|, then writes x = q' * scale / 128 *
-    // 2^(14 - e) as hi (row hh) and lo (row 8 + hh).  Heads past nh get zero rows.
-    auto rotate = [&](const uint16_t *v, float &a, float &c) {
-        a = (float)__builtin_bit_cast(_Float16, v[lane]);
-        c = (float)__builtin_bit_cast(_Float16, v[64 + lane]);
-        const float s0 = a + c;
-        c = a - c;
-        a = s0;
-#pragma unroll
-        for (int h = 32; h >= 1; h >>= 1) {
-            const float pa = __shfl_xor(a, h, 64), pc = __shfl_xor(c, h, 64);
-            const bool up = (lane & (uint32_t)h) != 0u;
-            a = up ? pa - a : a + pa;
-            c = up ? pc - c : c + pc;
-        }
-    };
-    for (uint32_t hh = wave; hh < (uint32_t)kQkHeads; hh += kWavesPerGroup) {
-        _Float16 *hi_row = qa + hh * kBlock, *lo_row = qa + (kQkHeads + hh) * kBlock;
-        if (hh < nh) {
-            const uint16_t *qv = q + ((size_t)b * Hq + h0 + hh) * ((size_t)m * kBlock);
-            float mx = 0.0f, a1 = 0.0f, c1 = 0.0f;   // a1, c1: the single slice when m == 1
-            for (uint32_t j = 0; j < m; ++j) {
-                float a, c;
-                rotate(qv + j * kBlock, a, c);
-                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(c)));
-                a1 = a;
-                c1 = c;
-            }
-#pragma unroll
-            for (int h = 32; h >= 1; h >>= 1)
-                mx = __builtin_fmaxf(mx, __shfl_xor(mx, h, 64));
-            int e = 0;
-            (void)frexpf(mx * __builtin_fabsf(scale) * (1.0f / 128.0f), &e);
-            const float f = ldexpf(scale * (1.0f / 128.0f), 14 - e);
-            for (uint32_t j = 0; j < m; ++j) {
-                float a = a1, c = c1;
-                if (!ONE_BLOCK)
-                    rotate(qv + j * kBlock, a, c);
-                _Float16 ah, al, ch, cl;
-                split_f16(a * f, ah, al);
-                split_f16(c * f, ch, cl);
-                hi_row[j * 2048 + lane] = ah;
-                hi_row[j * 2048 + 64 + lane] = ch;
-                lo_row[j * 2048 + lane] = al;
-                lo_row[j * 2048 + 64 + lane] = cl;
-            }
-            if (lane == 0)
-                pw_s[hh] = ldexpf(1.0f, e - 14);
-        } else {
-            for (uint32_t j = 0; j < m; ++j) {
-                hi_row[j * 2048 + lane] = hi_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
-                lo_row[j * 2048 + lane] = lo_row[j * 2048 + 64 + lane] = (_Float16)0.0f;
-            }
-            if (lane == 0)
-                pw_s[hh] = 0.0f;
-        }
-    }
+    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale);
     __syncthreads();
 
     // A operands of block j for this lane's row (lane % 16) and value run
@@ -888,38 +949,15 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             if constexpr (!ONE_BLOCK)
                 load_a(j, A);
             const uint32_t *w = wc[d];
-            // two accumulation chains (even / odd chunks) halve the dependent MFMA latency
-            f4_t D[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                u4_t bv;
-                if constexpr (BITS == 3) {
-                    uint32_t o[2];   // LDS addresses of the entries of v0 v1 and v2 v3
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const int bit = 12 * c + 6 * k2, wi = bit >> 5, sh = bit & 31;
-                        const uint32_t e = sh <= 26
-                                               ? __builtin_amdgcn_ubfe(w[wi], sh, 6)
-                                               : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 63u;
-                        o[k2] = lshl_add<ES>(e, tcopy);   // e * NC * EB + copy
-                    }
-                    const uint64_t r0 = lds_load<uint64_t>(o[0]), r1 = lds_load<uint64_t>(o[1]);
-                    bv = u4_t{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)};
-                } else {
-                    const uint32_t e = __builtin_amdgcn_ubfe(w[c >> 2], 8 * (c & 3), 8);
-                    bv = lds_load<u4_t>(lshl_add<ES>(e, tcopy));
-                }
-                D[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[c], __builtin_bit_cast(h8_t, bv),
-                                                                  D[c & 1], 0, 0, 0);
-            }
             uint16_t nr16 = nc[d];
             if constexpr (ONE_BLOCK)
                 nr16 = (uint16_t)__shfl((int)(d < 4 ? nca : ncb), 16 * (d & 3) + (int)n, 64);
             const float nf = (float)__builtin_bit_cast(_Float16, nr16);
+            const f4_t Du = qk_unit<BITS>(A, w, tcopy);
             if constexpr (ONE_BLOCK)
-                acc = (D[0] + D[1]) * nf;
+                acc = Du * nf;
             else
-                acc += (D[0] + D[1]) * nf;
+                acc += Du * nf;
             if (ONE_BLOCK || j == m - 1u) {
                 // rows h (hi) and 8 + h (lo) sit in lanes l and l + 32: one swap pairs them
                 float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
@@ -938,6 +976,419 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             }
         }
     }
+}
+
+// ---------------------------------------------------------------- decode attention
+//
+// out[b, h, :] = sum_t p_t v_hat_t with p = softmax_t(scale q . k_hat_t) over cache rows
+// [0, T): the fused read carried through softmax and the values.  Since
+// v_hat_t = (n_t / 128) H y_t and H is linear,
+//   sum_t p_t v_hat_t = H (sum_t p_t n_t y_t) / 128,
+// so the values are summed in the rotated domain and transformed once per head.
+//
+// attn_partial_kernel: a workgroup takes one (sequence, kv head, <= 8 query heads) and
+// a chunk of rows; each wave scores its own rows exactly as qk_kernel does, keeps an
+// online softmax per head (running max m, running sum l of exp(s - m)) and accumulates
+// acc = sum_t exp(s_t - m) n_t y_t; the four waves' states are merged in LDS and the
+// workgroup writes one (m, l, acc) per head to the workspace.  attn_combine_kernel:
+// one workgroup per (sequence, query head) merges the chunks, transforms acc once and
+// divides by 128 l.
+//
+// P.V runs on the matrix cores too: v_mfma_f32_16x16x32_f16 with A = the weights
+// (rows 0..7 the fp16 hi parts of the 8 heads' w_t = exp(s_t - m) n_t 2^(15 - E), rows 8..15
+// their lo parts) and B = the levels (yh, yl) of 16 value positions, contracted over
+// the 16 rows (tokens) of a unit, each token taking two products, w yh and w yl.
+// Column c' of product block c stands for value position 8 c' + c, so the lane of
+// column c' needs values 8 c' .. 8 c' + 7 of its four tokens: eight codes that are one
+// contiguous 24-bit (turbo3) / 16-bit (turbo2) field of each token's packed block.
+// Each wave parks its 16 tokens' packed codes in a small LDS tile (a 48-byte row per
+// token) and every lane reads its four fields from it and looks the code pairs up.
+// The weights are written to a small LDS tile by the lanes that computed them (two
+// (head, token) pairs each) and read back in the A layout.  The softmax runs once per
+// batch of four units (64 rows): one running-max update, one sum and one wave
+// barrier for the batch's tiles.  w = exp(s - m) n 2^(15 - E), with E the exponent of
+// the largest value norm seen so far, lies below 2^15, inside fp16's range, and keeps
+// the lo part a normal number down to weights 2^-18 of the largest: the weights that
+// follow a dominant row (on a row of zeros, say) keep their relative precision.  A
+// larger E rescales acc by a power of two, the way a larger score rescales it by
+// exp(m_old - m_new).
+
+constexpr int kAttnDepth = 4;          // 16-row units in flight per wave
+constexpr int kAttnGroupsPerCu = 2;    // the target of the row chunking
+constexpr int kAttnRaw = 16 * 48;      // bytes of a wave's packed-code tile (16 rows)
+constexpr int kAttnRec = 4 + kBlock;   // workspace floats per partial: m, l, -, -, acc[128]
+constexpr int kAttnWExp = 15;          // the weights' power-of-two headroom below fp16's max
+
+// Value lookup table: entry e (two codes, the first in the low bits) -> the dwords
+// (yh0 | yl0 << 16, yh1 | yl1 << 16), kLdsCopies8 copies.
+constexpr int attn_vtable_bytes(int bits) { return (1 << (2 * bits)) * kLdsCopies8 * 8; }
+
+template <int BITS>
+__global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
+    const uint8_t *__restrict__ k_codes, const uint16_t *__restrict__ k_norms,
+    const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
+    const uint16_t *__restrict__ q, float *__restrict__ work, uint32_t Hkv, int64_t Tc,
+    uint32_t T, uint32_t G, uint32_t Hq, uint32_t passes, uint32_t tpg, uint32_t nparts,
+    float scale, Codebook cb)
+{
+    constexpr int NC = QkTable<BITS>::NC, EB = QkTable<BITS>::EB;
+    constexpr int CB = 16 * BITS;   // code bytes per block
+    constexpr int LW = BITS;        // code words per lane (32 codes)
+    constexpr int VNE = 1 << (2 * BITS);
+    constexpr int kTables = qk_table_bytes(BITS) + attn_vtable_bytes(BITS);
+    constexpr int kMerge = kWavesPerGroup * kQkHeads * (kBlock + 2) * 4;   // after the rows
+    static_assert(kMerge <= kTables, "the merge reuses the tables' bytes");
+    // the K and V tables, then (after the last unit) the four waves' states
+    __shared__ __attribute__((aligned(16))) uint8_t tables[kTables];
+    __shared__ __attribute__((aligned(16))) _Float16 qa[16 * kBlock];
+    // per unit in flight: the packed value codes of its 16 rows (48-byte rows, one
+    // spare dword read past the last field) and the weights [head][row]
+    __shared__ __attribute__((aligned(16))) uint32_t raw[kAttnDepth][kWavesPerGroup][kAttnRaw / 4 + 4];
+    __shared__ __attribute__((aligned(16))) float ptile[kAttnDepth][kWavesPerGroup][kQkHeads * 16];
+    __shared__ __attribute__((aligned(16))) float ftile[kWavesPerGroup][kQkHeads];
+    __shared__ float pw_s[kQkHeads];
+    __shared__ float lv[8];
+    uint8_t *ktable = tables, *vtable = tables + qk_table_bytes(BITS);
+
+    const uint32_t pass = blockIdx.x % passes;
+    const uint32_t bg = blockIdx.x / passes;           // b * Hkv + g
+    const uint32_t b = bg / Hkv, g = bg - b * Hkv;
+    const uint32_t h0 = g * G + pass * kQkHeads;       // first query head of this pass
+    const uint32_t nh = min(G - pass * kQkHeads, (uint32_t)kQkHeads);
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n = lane & 15u, part = lane >> 4;
+    const uint32_t t_begin = blockIdx.y * tpg;
+    const uint32_t t_end = min(T, t_begin + tpg);
+    const size_t row0 = (size_t)bg * Tc;
+
+    // this wave's rows [first, last); unit k covers rows first + 16 k + [0, 16)
+    const uint32_t wspan = tpg / kWavesPerGroup;
+    const uint32_t first = t_begin + wave * wspan;
+    const uint32_t last = min(t_end, first + wspan);
+    const uint32_t nunits = first < last ? (last - first + 15u) / 16u : 0u;
+
+    // K and V codes of this lane's run (row n, values 32 part ..) of unit k, and a
+    // batch's norms (row first + 16 k + lane, one per lane: kAttnDepth units = 64 rows);
+    // loads unconditional as in qk_kernel (rows past the wave's range read valid rows
+    // and are never used)
+    auto fetch = [&](uint32_t k, uint32_t (&wk)[LW], uint32_t (&wv)[LW]) {
+        const uint32_t tb = min(first + k * 16u, t_end - 1u);
+        const uint32_t r = min(n, t_end - 1u - tb);
+        const size_t off = (row0 + tb) * CB + (__umul24(r, (uint32_t)CB) + part * (4 * BITS));
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            wk[i] = ld_stream((const uint32_t *)(k_codes + off) + i);
+            wv[i] = ld_stream((const uint32_t *)(v_codes + off) + i);
+        }
+    };
+    static_assert(kAttnDepth * 16 == 64, "one norm load per lane per batch");
+    static_assert(kAttnDepth % 2 == 0, "tiles alternate between units");
+    auto fetch_norms = [&](uint32_t k, uint32_t &nk, uint32_t &nv) {
+        const uint32_t t = min(first + 16u * k + lane, t_end - 1u);
+        nk = ld_stream(k_norms + row0 + t);
+        nv = ld_stream(v_norms + row0 + t);
+    };
+    uint32_t wkn[kAttnDepth][LW], wvn[kAttnDepth][LW];
+    uint32_t nkn = 0, nvn = 0;
+#pragma unroll
+    for (int d = 0; d < kAttnDepth; ++d)
+        fetch(d, wkn[d], wvn[d]);
+    fetch_norms(0, nkn, nvn);
+
+    // tables and query operands
+    levels_to_lds(lv, cb);
+    __syncthreads();
+    qk_fill_table<BITS>(ktable, lv);
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(VNE * kLdsCopies8); i += blockDim.x) {
+        const uint32_t e = i / kLdsCopies8;
+        _Float16 a0, c0, a1, c1;
+        split_f16(lv[e & ((1u << BITS) - 1u)], a0, c0);
+        split_f16(lv[e >> BITS], a1, c1);
+        *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, c0), pack_h2(a1, c1)};
+    }
+    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale);
+    __syncthreads();
+
+    h8_t A[8];
+    {
+        const _Float16 *arow = qa + n * kBlock + part * 32;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t *p = (const uint32_t *)(arow + 4 * c);
+            const uint32_t x01 = p[0], x23 = p[1];
+            A[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
+        }
+    }
+    const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)ktable + (lane % NC) * EB;
+    const uint32_t vcopy = (uint32_t)(uintptr_t)(lds_u8 *)vtable + (lane % kLdsCopies8) * 8;
+    // after the hi/lo combine, lane l holds heads hu and hu + 2 of token l % 16
+    const uint32_t hu = 4u * (part & 1u) + (lane >> 5);
+    const float pw_u = pw_s[hu], pw_v = pw_s[hu + 2];
+    float *ft = ftile[wave];
+    // this lane's 8-value field in a token row of the code tile (column n: values
+    // 8 n .. 8 n + 7): dwords dA, dA + 1 of the row, shifted by fsh
+    constexpr int FBITS = 8 * BITS;
+    const uint32_t dA = (FBITS * n) >> 5, fsh = (FBITS * n) & 31u;
+
+    // online softmax state: running max and sum of heads hu, hu + 2 (the same in all 16
+    // lanes of a row), the value-norm exponent E (wave-wide) and the P.V accumulators
+    // (rows 4 (lane / 16) .. + 3 = heads hi / lo, column lane % 16 of value block c)
+    float m_u = -__builtin_inff(), m_v = -__builtin_inff(), l_u = 0.0f, l_v = 0.0f;
+    int E = -1000;
+    f4_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        acc[c] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // max / sum over the 16 lanes of a row (one token each)
+    auto row_max = [](float x) {
+        x = __builtin_fmaxf(x, dpp_f32<0xB1>(x));
+        x = __builtin_fmaxf(x, dpp_f32<0x4E>(x));
+        x = __builtin_fmaxf(x, dpp_f32<0x124>(x));   // row_ror:4
+        x = __builtin_fmaxf(x, dpp_f32<0x128>(x));   // row_ror:8
+        return x;
+    };
+    auto row_sum = [](float x) {
+        x += dpp_f32<0xB1>(x);
+        x += dpp_f32<0x4E>(x);
+        x += dpp_f32<0x124>(x);
+        x += dpp_f32<0x128>(x);
+        return x;
+    };
+
+    for (uint32_t k0 = 0; k0 < nunits; k0 += kAttnDepth) {
+        uint32_t wkc[kAttnDepth][LW], wvc[kAttnDepth][LW];
+#pragma unroll
+        for (int d = 0; d < kAttnDepth; ++d)
+#pragma unroll
+            for (int i = 0; i < LW; ++i) {
+                wkc[d][i] = wkn[d][i];
+                wvc[d][i] = wvn[d][i];
+            }
+        const uint32_t nkc = nkn, nvc = nvn;
+        if (k0 + kAttnDepth < nunits) {
+#pragma unroll
+            for (int d = 0; d < kAttnDepth; ++d)
+                fetch(k0 + kAttnDepth + d, wkn[d], wvn[d]);
+            fetch_norms(k0 + kAttnDepth, nkn, nvn);
+        }
+        // scores of heads hu, hu + 2 for token n of each unit (as qk_kernel), -inf past
+        // the range; the units' packed value codes into their tiles (row n, bytes
+        // 4 BITS part ..)
+        float su[kAttnDepth], sv[kAttnDepth], nvd[kAttnDepth];
+        float bu = -__builtin_inff(), bv = -__builtin_inff(), bn = 0.0f;
+#pragma unroll
+        for (int d = 0; d < kAttnDepth; ++d) {
+            uint32_t *rt = raw[d][wave];
+#pragma unroll
+            for (int i = 0; i < LW; ++i)
+                rt[n * 12 + part * LW + i] = wvc[d][i];
+            const f4_t Du = qk_unit<BITS>(A, wkc[d], tcopy);
+            const uint16_t nk16 = (uint16_t)__shfl((int)nkc, 16 * d + (int)n, 64);
+            const uint16_t nv16 = (uint16_t)__shfl((int)nvc, 16 * d + (int)n, 64);
+            const f4_t sc = Du * (float)__builtin_bit_cast(_Float16, nk16);
+            float s0 = sc[0], s1 = sc[1], s2 = sc[2], s3 = sc[3];
+            swap32(s0, s1);
+            swap32(s2, s3);
+            const bool live = first + 16u * (k0 + d) + n < last;
+            su[d] = live ? (s0 + s1) * pw_u : -__builtin_inff();
+            sv[d] = live ? (s2 + s3) * pw_v : -__builtin_inff();
+            nvd[d] = (float)__builtin_bit_cast(_Float16, nv16);
+            bu = __builtin_fmaxf(bu, su[d]);
+            bv = __builtin_fmaxf(bv, sv[d]);
+            bn = __builtin_fmaxf(bn, live ? nvd[d] : 0.0f);
+        }
+        // online softmax over the batch's 64 rows (unit k0 holds a live row, so the
+        // maxima are finite); the value-norm exponent follows the largest norm so far
+        const float mu = __builtin_fmaxf(m_u, row_max(bu));
+        const float mv = __builtin_fmaxf(m_v, row_max(bv));
+        const float au = __expf(m_u - mu), av = __expf(m_v - mv);
+        int eu = 0;
+        (void)frexpf(row_max(bn), &eu);
+        const int En = max(E, __builtin_amdgcn_readfirstlane(eu));
+        float ru = 0.0f, rv = 0.0f;
+#pragma unroll
+        for (int d = 0; d < kAttnDepth; ++d) {
+            const float pu = __expf(su[d] - mu), pv = __expf(sv[d] - mv);
+            ru += pu;
+            rv += pv;
+            float *pt = ptile[d][wave];
+            pt[hu * 16 + n] = ldexpf(pu * nvd[d], kAttnWExp - En);
+            pt[(hu + 2) * 16 + n] = ldexpf(pv * nvd[d], kAttnWExp - En);
+        }
+        l_u = l_u * au + row_sum(ru);
+        l_v = l_v * av + row_sum(rv);
+        m_u = mu;
+        m_v = mv;
+        const bool resc = __any(au != 1.0f || av != 1.0f) || En != E;
+        if (resc) {   // scale acc rows by their head's exp(m_old - m_new) 2^(E_old - E_new)
+            const float sE = ldexpf(1.0f, E - En);
+            if (n == 0) {
+                ft[hu] = au * sE;
+                ft[hu + 2] = av * sE;
+            }
+            wave_lds_sync();
+            const float4 f4 = *(const float4 *)(ft + 4 * (part & 1u));
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = acc[c] * f4_t{f4.x, f4.y, f4.z, f4.w};
+        }
+        E = En;
+        wave_lds_sync();   // weights and code tiles complete
+#pragma unroll
+        for (int d = 0; d < kAttnDepth; ++d) {
+            const uint32_t *rt = raw[d][wave];
+            const float *pt = ptile[d][wave];
+            // A: row lane % 16 = head (lane % 8), hi (rows 0..7) or lo (8..15) part of
+            // the weights of tokens 4 (lane / 16) .. + 3, each twice (for yh and yl)
+            h8_t Ap;
+            {
+                const float4 x = *(const float4 *)(pt + (n & 7u) * 16 + 4 * part);
+                const float xv[4] = {x.x, x.y, x.z, x.w};
+                uint32_t hw[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    _Float16 hi, lo;
+                    split_f16(xv[k], hi, lo);
+                    const _Float16 sel = n < 8 ? hi : lo;
+                    hw[k] = pack_h2(sel, sel);
+                }
+                Ap = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], hw[2], hw[3]});
+            }
+            // B: values 8 n + c of tokens 4 (lane / 16) .. + 3, two values per lookup
+            uint64_t ent[4][4];   // [token][pair j]: values 8 n + 2 j, 8 n + 2 j + 1
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t *row = rt + (4 * part + k) * 12 + dA;
+                const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e = __builtin_amdgcn_ubfe(f, 2 * BITS * j, 2 * BITS);
+                    ent[k][j] = lds_load<uint64_t>(lshl_add<8>(e, vcopy));
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int j = c >> 1, sh = 32 * (c & 1);
+                const u4_t bv = u4_t{(uint32_t)(ent[0][j] >> sh), (uint32_t)(ent[1][j] >> sh),
+                                     (uint32_t)(ent[2][j] >> sh), (uint32_t)(ent[3][j] >> sh)};
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap, __builtin_bit_cast(h8_t, bv),
+                                                                acc[c], 0, 0, 0);
+            }
+        }
+    }
+
+    // this wave's state: rows h (hi) and 8 + h (lo) of acc sit in lanes l and l + 32;
+    // value 8 n + c of heads hu, hu + 2; into LDS (over the tables), then merged
+    __syncthreads();   // every wave is done with the tables
+    float *mg = (float *)tables;   // [wave][head][2 + 128]
+    {
+        float ou[8], ov[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float a0 = acc[c][0], a1 = acc[c][1], a2 = acc[c][2], a3 = acc[c][3];
+            swap32(a0, a1);
+            swap32(a2, a3);
+            ou[c] = ldexpf(a0 + a1, E - kAttnWExp);
+            ov[c] = ldexpf(a2 + a3, E - kAttnWExp);
+        }
+        float *ru = mg + (wave * kQkHeads + hu) * (kBlock + 2);
+        float *rv = mg + (wave * kQkHeads + hu + 2) * (kBlock + 2);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            ru[2 + 8 * n + c] = ou[c];
+            rv[2 + 8 * n + c] = ov[c];
+        }
+        if (n == 0) {
+            ru[0] = m_u;
+            ru[1] = l_u;
+            rv[0] = m_v;
+            rv[1] = l_v;
+        }
+    }
+    __syncthreads();
+    {
+        // thread -> head threadIdx / 32, values 4 (threadIdx % 32) .. + 3
+        const uint32_t h = threadIdx.x >> 5, v0 = 4u * (threadIdx.x & 31u);
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w)
+            M = __builtin_fmaxf(M, mg[(w * kQkHeads + h) * (kBlock + 2)]);
+        float L = 0.0f, a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+            const float *r = mg + (w * kQkHeads + h) * (kBlock + 2);
+            const float f = r[0] == -__builtin_inff() ? 0.0f : __expf(r[0] - M);
+            L += f * r[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] += f * r[2 + v0 + i];
+        }
+        if (h < nh) {
+            float *rec = work + (((size_t)b * Hq + h0 + h) * nparts + blockIdx.y) * kAttnRec;
+            *(float4 *)(rec + 4 + v0) = float4{a[0], a[1], a[2], a[3]};
+            if (v0 == 0) {
+                rec[0] = M;
+                rec[1] = L;
+            }
+        }
+    }
+}
+
+// One workgroup per (sequence, query head): merge the chunks' partials (wave w takes
+// chunks w, w + 4, ...; lane l values l and 64 + l), add the four waves, transform
+// once and divide by 128 l.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ work,
+                                                           float *__restrict__ out,
+                                                           uint32_t nparts)
+{
+    __shared__ float red[kWavesPerGroup][kBlock + 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t bh = blockIdx.x;
+    const float *rec = work + (size_t)bh * nparts * kAttnRec;
+    // the largest running max over all chunks (every wave computes it)
+    float M = -__builtin_inff();
+    for (uint32_t p = lane; p < nparts; p += 64)
+        M = __builtin_fmaxf(M, rec[(size_t)p * kAttnRec]);
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1)
+        M = __builtin_fmaxf(M, __shfl_xor(M, h, 64));
+    float L = 0.0f, a = 0.0f, c = 0.0f;
+#pragma unroll 4
+    for (uint32_t p = wave; p < nparts; p += kWavesPerGroup) {
+        const float *r = rec + (size_t)p * kAttnRec;
+        const float w = __expf(r[0] - M);   // every chunk holds a row: r[0] is finite
+        L += w * r[1];
+        a += w * r[4 + lane];
+        c += w * r[68 + lane];
+    }
+    red[wave][lane] = a;
+    red[wave][64 + lane] = c;
+    if (lane == 0)
+        red[wave][kBlock] = L;
+    __syncthreads();
+    if (wave != 0)
+        return;
+    a = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    c = red[0][64 + lane] + red[1][64 + lane] + red[2][64 + lane] + red[3][64 + lane];
+    L = red[0][kBlock] + red[1][kBlock] + red[2][kBlock] + red[3][kBlock];
+    // H: span 64 in-lane, spans 32..1 across lanes
+    const float s0 = a + c;
+    c = a - c;
+    a = s0;
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+        const float pa = __shfl_xor(a, h, 64), pc = __shfl_xor(c, h, 64);
+        const bool up = (lane & (uint32_t)h) != 0u;
+        a = up ? pa - a : a + pa;
+        c = up ? pc - c : c + pc;
+    }
+    const float inv = 1.0f / (128.0f * L);
+    out[(size_t)bh * kBlock + lane] = a * inv;
+    out[(size_t)bh * kBlock + 64 + lane] = c * inv;
 }
 
 // Compute units of the current device (cached per device).
@@ -1060,6 +1511,58 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
     if (bits == 3)
         return m == 1 ? launch(qk_kernel<3, true>) : launch(qk_kernel<3, false>);
     return m == 1 ? launch(qk_kernel<2, true>) : launch(qk_kernel<2, false>);
+}
+
+
+// Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
+// device): about kAttnGroupsPerCu workgroups per CU of a 256-CU MI355X, whole batches of
+// kAttnDepth units per wave, at most 65535 chunks.
+int64_t attn_chunk_rows(int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+{
+    const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
+    const int64_t step = (int64_t)kWavesPerGroup * 16 * kAttnDepth;
+    const int64_t round = 256 * kAttnGroupsPerCu;
+    int64_t rows = (T * B * Hkv * passes + round - 1) / round;
+    rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
+    rows = ((rows + step - 1) / step) * step;
+    return rows < step ? step : rows;
+}
+
+int64_t attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+{
+    const int64_t chunks = (T + attn_chunk_rows(B, Hkv, T, Hq) - 1) / attn_chunk_rows(B, Hkv, T, Hq);
+    return B * Hq * chunks * kAttnRec * (int64_t)sizeof(float);
+}
+
+int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *v_codes,
+                const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t T,
+                const void *q, int64_t Hq, float scale, float *out, void *work, void *stream)
+{
+    const Codebook *cb = codebook(bits);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
+    const int64_t rows = attn_chunk_rows(B, Hkv, T, Hq);
+    const int64_t chunks = (T + rows - 1) / rows;
+    const uint32_t nparts = (uint32_t)chunks;
+    dim3 grid((uint32_t)(B * Hkv * passes), (uint32_t)chunks), block(256);
+    if (bits == 3)
+        hipLaunchKernelGGL(attn_partial_kernel<3>, grid, block, 0, s, (const uint8_t *)k_codes,
+                           (const uint16_t *)k_norms, (const uint8_t *)v_codes,
+                           (const uint16_t *)v_norms, (const uint16_t *)q, (float *)work,
+                           (uint32_t)Hkv, Tc, (uint32_t)T, (uint32_t)G, (uint32_t)Hq,
+                           (uint32_t)passes, (uint32_t)rows, nparts, scale, *cb);
+    else
+        hipLaunchKernelGGL(attn_partial_kernel<2>, grid, block, 0, s, (const uint8_t *)k_codes,
+                           (const uint16_t *)k_norms, (const uint8_t *)v_codes,
+                           (const uint16_t *)v_norms, (const uint16_t *)q, (float *)work,
+                           (uint32_t)Hkv, Tc, (uint32_t)T, (uint32_t)G, (uint32_t)Hq,
+                           (uint32_t)passes, (uint32_t)rows, nparts, scale, *cb);
+    int e = (int)hipGetLastError();
+    if (e)
+        return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
+                       (const float *)work, out, nparts);
+    return (int)hipGetLastError();
 }
 
 }  // namespace tq

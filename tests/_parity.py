@@ -16,7 +16,9 @@ Rules (readings of the tolerances, each applied element by element):
           one-hot outlier reconstructed at 1.51x) both sides must give the
           same infinity, the IEEE round-to-nearest result;
   scores  |g - r| <= 2e-3 * max(|r|, 0.01 * ||q|| * ||k_hat||), r the oracle's
-          scores over the GPU-written cache.
+          scores over the GPU-written cache;
+  attention |g - r| <= 2e-3 * max(|r|, 0.01 * rms(r over the head's 128 outputs)), r the
+          oracle's binary64 decode attention over the GPU-written K and V caches.
 """
 from __future__ import annotations
 
@@ -93,3 +95,22 @@ def check_scores(gpu, ref, qnorm, knorm, what=""):
     worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
     assert np.all(err <= tol), f"{what}: score error {worst:.3f} x tolerance"
     return {"scores_worst_over_tol": worst}
+
+
+def check_attn(gpu, ref, vmax, T, what=""):
+    """Decode attention [B, Hq, D]: 2e-3 of max(|r|, 1% of the head's rms), plus an
+    absolute floor T 2^-38 max|v_hat| (vmax [B, Hq], over the head's rows < T).  The
+    floor is the resolution of the weights' fp16 operands: each weight is carried to
+    2^-25 on a scale whose largest weight is 2^15, so rows far below the dominant one
+    contribute to about 2^-40 of the largest value each.  It only matters when the
+    output is many orders below the values, as when the softmax sits on a zero row."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    floor = T * 2.0 ** -38 * np.asarray(vmax, dtype=np.float64)[..., None]
+    tol = 2e-3 * np.maximum(np.abs(r), 0.01 * rms) + floor
+    err = np.abs(g - r)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    assert np.all(err <= tol), f"{what}: attention error {worst:.3f} x tolerance"
+    return {"attn_worst_over_tol": worst}

@@ -12,6 +12,7 @@ import kv_cache_quantization_block_amd as tq
 import oracle
 
 OK, E_TYPE, E_SHAPE, E_RANGE, E_NULL, E_ALIGN, E_ALIAS = 0, -1, -2, -3, -4, -5, -6
+E_WORKSPACE = -8
 
 
 @pytest.fixture(scope="module")
@@ -24,7 +25,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = tq.header_functions()
-    assert {"tq_encode", "tq_decode", "tq_qk_scores", "tq_codebook"} <= set(names)
+    assert {"tq_encode", "tq_decode", "tq_qk_scores", "tq_codebook", "tq_attn_decode",
+            "tq_attn_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -122,6 +124,52 @@ def test_qk_validation(L):
     assert call(o=ctypes.cast(ctypes.c_void_p(Q), ctypes.POINTER(ctypes.c_float))) == E_ALIAS
     assert call(B=0, c=None, n=None, q=None) == OK
     assert call(T=0) == OK
+
+
+def test_attn_workspace_bytes():
+    """Depends on the sizes only; 132 floats (m, l, two spare, 128 values) per partial,
+    one partial per row chunk of every (sequence, query head)."""
+    ws = tq.tq_attn_workspace_bytes
+    assert ws(3, 0, 8, 32768, 128, 32768, 32) == 0
+    n16 = ws(3, 16, 8, 32768, 128, 32768, 32)
+    assert n16 > 0 and n16 % (16 * 32 * 132 * 4) == 0
+    n1 = ws(2, 1, 8, 32768, 128, 32768, 32)
+    assert n1 > 0 and n1 % (32 * 132 * 4) == 0
+    with pytest.raises(tq.TQError):
+        ws(3, 1, 8, 100, 256, 100, 32)       # D != 128
+    with pytest.raises(tq.TQError):
+        ws(3, 1, 8, 100, 128, 0, 32)         # no rows
+    with pytest.raises(tq.TQError):
+        ws(3, 1, 8, 100, 128, 101, 32)       # T > Tc
+
+
+def test_attn_validation(L):
+    f = L.tq_attn_decode
+    S4 = ctypes.cast(ctypes.c_void_p(S), ctypes.POINTER(ctypes.c_float))
+    W = 0x60000000
+    need = tq.tq_attn_workspace_bytes(3, 1, 2, 8, 128, 8, 8)
+    args = lambda **kw: dict(dict(t=3, kc=_p(C), kn=_p(N), vc=_p(C + 0x1000000), vn=_p(N + 0x1000000),
+                                  B=1, Hkv=2, Tc=8, D=128, T=8, q=_p(Q), Hq=8, s=ctypes.c_float(1.0),
+                                  o=S4, w=_p(W), wb=need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["t"], a["kc"], a["kn"], a["vc"], a["vn"], a["B"], a["Hkv"], a["Tc"], a["D"],
+                 a["T"], a["q"], a["Hq"], a["s"], a["o"], a["w"], a["wb"], None)
+
+    assert call(t=1) == E_TYPE
+    assert call(Hq=7) == E_SHAPE
+    assert call(D=256) == E_SHAPE
+    assert call(T=0) == E_SHAPE
+    assert call(T=9) == E_RANGE
+    assert call(vc=None) == E_NULL
+    assert call(w=None) == E_NULL
+    assert call(vn=_p(N + 1)) == E_ALIGN
+    assert call(w=_p(W + 8)) == E_ALIGN
+    assert call(wb=need - 1) == E_WORKSPACE
+    assert call(o=ctypes.cast(ctypes.c_void_p(C), ctypes.POINTER(ctypes.c_float))) == E_ALIAS
+    assert call(w=_p(S)) == E_ALIAS
+    assert call(B=0, kc=None, kn=None, vc=None, vn=None, q=None, w=None) == OK
 
 
 def test_codebook_validation(L):

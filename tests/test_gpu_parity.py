@@ -13,7 +13,7 @@ import torch
 import gen
 import kv_cache_quantization_block_amd as tq
 import oracle
-from _parity import check_codes, check_decode, check_norms, check_scores, unpack_codes
+from _parity import check_attn, check_codes, check_decode, check_norms, check_scores, unpack_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +198,57 @@ def test_qk_query_magnitudes(bits):
     mul = [1e-4, 3e-3, 1.0, 40.0, 3e3, 0.5, 1e-2, 7.0]
     print(_qk_case(bits, 1, 2, 4, 300, 300, 128, seed=77, q_mul=mul))
     print(_qk_case(bits, 1, 1, 3, 64, 64, 256, seed=78, scale=-0.37))
+
+
+# ---------------------------------------------------------------- decode attention
+
+def _attn_case(bits, B, Hkv, G, Tc, T, seed, q_mul=1.0, scale=None, v_mul=1.0, zero_rows=()):
+    k = _rand_kv(seed, B, Hkv, Tc, 128)
+    v = _rand_kv(seed + 7, B, Hkv, Tc, 128)
+    v = (v.double() * v_mul).half()
+    for t in zero_rows:
+        v[:, :, t] = 0
+    kc, kn = _gpu_encode(bits, k, Tc, 0)
+    vc, vn = _gpu_encode(bits, v, Tc, 0)
+    q = (gen.queries(seed + 1, B, Hkv * G, 128).double() * q_mul).half()
+    assert bool(torch.isfinite(q).all()) and bool(torch.isfinite(v).all())
+    scale = 1.0 / math.sqrt(128) if scale is None else scale
+    out = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    tq.tq_attn_decode(bits, kc, kn, vc, vn, q.cuda(), scale, out, T=T)
+    torch.cuda.synchronize()
+    vcn, vnn = vc.cpu().numpy(), vn.cpu().numpy()
+    ref = oracle.attn_decode(bits, kc.cpu().numpy(), kn.cpu().numpy(), vcn, vnn, q.numpy(), scale, T=T)
+    vhat = oracle.decode_blocks(bits, vcn[:, :, :T].reshape(-1, 16 * bits), vnn[:, :, :T].reshape(-1))[0]
+    vmax = np.repeat(np.abs(vhat).reshape(B, Hkv, -1).max(axis=-1), G, axis=1)
+    return check_attn(out.cpu().numpy(), ref, vmax, T, f"attn bits={bits} B={B} Hkv={Hkv} G={G} T={T}")
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("case", [
+    (1, 2, 4, 100, 97),      # GQA group 4, ragged T < Tc
+    (2, 1, 8, 40, 33),       # group 8: one full pass
+    (1, 1, 12, 300, 300),    # group 12: passes of eight and four heads
+    (1, 3, 1, 70, 70),       # no grouping
+    (1, 2, 2, 1, 1),         # one row: the output is that row's value
+    (1, 2, 4, 5000, 4999),   # many row chunks and waves, ragged last unit
+    (3, 2, 4, 2000, 1500),   # several sequences, T well below Tc
+])
+def test_attn_decode(bits, case):
+    B, Hkv, G, Tc, T = case
+    print(_attn_case(bits, B, Hkv, G, Tc, T, seed=41 + G + T % 97))
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_attn_decode_extremes(bits):
+    """A peaked softmax (large scale), a nearly flat one (tiny scale), value norms from
+    1e-4 to 30 times the usual and all-zero value rows, also under a softmax whose
+    largest weights sit on zero rows (outputs many orders below the values, down to
+    about 1e-155 of them): the running maximum and the power-of-two weight scaling
+    keep every head within the bound."""
+    print(_attn_case(bits, 1, 2, 4, 600, 600, seed=51, scale=2.0))
+    print(_attn_case(bits, 1, 2, 4, 600, 600, seed=52, scale=1e-4))
+    print(_attn_case(bits, 1, 2, 4, 600, 590, seed=53, v_mul=1e-4))
+    print(_attn_case(bits, 1, 2, 4, 600, 600, seed=54, v_mul=30.0, q_mul=3.0))
+    print(_attn_case(bits, 1, 2, 4, 300, 300, seed=55, zero_rows=range(0, 300, 3)))
+    print(_attn_case(bits, 1, 2, 4, 300, 300, seed=60, scale=0.3, zero_rows=range(1, 300, 2)))
+    print(_attn_case(bits, 1, 2, 4, 300, 300, seed=57, scale=2.0, zero_rows=range(1, 300, 2)))
