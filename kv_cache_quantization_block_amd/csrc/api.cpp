@@ -218,7 +218,7 @@ int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, in
         return st;
     if (B == 0)
         return 0;
-    return tq::attn_workspace_bytes(B, Hkv, T, Hq);
+    return tq::attn_workspace_bytes(type, B, Hkv, T, Hq);
 }
 
 int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
@@ -238,7 +238,7 @@ int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const voi
         !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(out, 4) ||
         !aligned(workspace, 16))
         return TQ_ERR_ALIGN;
-    const int64_t need = tq::attn_workspace_bytes(B, Hkv, T, Hq);
+    const int64_t need = tq::attn_workspace_bytes(type, B, Hkv, T, Hq);
     if (workspace_bytes < need)
         return TQ_ERR_WORKSPACE;
     const int64_t ob = B * Hq * D * 4, cb = cache_blocks * 16 * type, nb = cache_blocks * 2;

@@ -46,8 +46,8 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
 
 // Decode attention (D = 128): rows per chunk and workspace bytes follow from the sizes
 // alone; the launch runs the partial and the combine kernel.
-int64_t attn_chunk_rows(int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
-int64_t attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
+int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
+int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
 int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *v_codes,
                 const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t T,
                 const void *q, int64_t Hq, float scale, float *out, void *work, void *stream);

@@ -111,6 +111,40 @@ __device__ __forceinline__ float dpp_f32(float v)
                                                                  0xF, 0xF, false));
 }
 
+// Max / sum over each row of 16 lanes, one DPP ALU instruction per step (the builtin
+// route adds a zeroing move and a canonicalising max to each step).  Two wait states
+// precede each DPP read of a VGPR that a VALU instruction may just have written.
+__device__ __forceinline__ float row16_max(float x)
+{
+    float r;
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "=&v"(r)
+        : "v"(x));
+    return r;
+}
+__device__ __forceinline__ float row16_sum(float x)
+{
+    float r;
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "=&v"(r)
+        : "v"(x));
+    return r;
+}
+
 // (a << S) + b as one v_lshl_add_u32 (kept as written: the compiler would otherwise
 // re-associate a chain of these into more instructions).
 template <int S>
@@ -667,6 +701,14 @@ __device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
     lo = (_Float16)(x - (float)hi);
 }
 
+// x as packed fp16 (hi, lo): hi = fp16(x), lo = fp16(x - hi) rounded toward zero (hi
+// is exact in fp16, so the truncating pack keeps it).
+__device__ __forceinline__ uint32_t split_pack(float x)
+{
+    const float hi = (float)(_Float16)x;
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi, x - hi));
+}
+
 
 // The q.K table (two-value entries for turbo3, four-value for turbo2): entry e,
 // copy c at (e * NC + c) * EB; lane l reads copy l % NC.
@@ -994,17 +1036,25 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 // one workgroup per (sequence, query head) merges the chunks, transforms acc once and
 // divides by 128 l.
 //
-// P.V runs on the matrix cores too: v_mfma_f32_16x16x32_f16 with A = the weights
-// (rows 0..7 the fp16 hi parts of the 8 heads' w_t = exp(s_t - m) n_t 2^(15 - E), rows 8..15
-// their lo parts) and B = the levels (yh, yl) of 16 value positions, contracted over
-// the 16 rows (tokens) of a unit, each token taking two products, w yh and w yl.
-// Column c' of product block c stands for value position 8 c' + c, so the lane of
-// column c' needs values 8 c' .. 8 c' + 7 of its four tokens: eight codes that are one
-// contiguous 24-bit (turbo3) / 16-bit (turbo2) field of each token's packed block.
-// Each wave parks its 16 tokens' packed codes in a small LDS tile (a 48-byte row per
-// token) and every lane reads its four fields from it and looks the code pairs up.
-// The weights are written to a small LDS tile by the lanes that computed them (two
-// (head, token) pairs each) and read back in the A layout.  The softmax runs once per
+// P.V runs on the matrix cores too: v_mfma_f32_16x16x32_f16 over the 16 rows (tokens)
+// of a unit, for a set of four query heads.  Row r = 8 hilo + 2 hh + e of A stands for
+// head hh of the set, value-position parity e and the fp16 hi (hilo 0) or lo (1) part
+// of the weight w_t = exp(s_t - m) n_t 2^(15 - E); k-slots 8 j .. 8 j + 7 (lane group j)
+// are tokens 2 j and 2 j + 1 of an 8-token block, each as (yh of parity 0, yh of
+// parity 1, yl of parity 0, yl of parity 1).  A holds w in the slots of its own parity
+// and zeros in the others, so column P of the product is sum_t w_t y_t at position
+// 2 P + e in row e: the two positions of a pair take one row each.  That B layout is
+// exactly what a two-code q.K table entry (positions 2 P, 2 P + 1 of one token) holds,
+// so two lookups (tokens 2 j, 2 j + 1) fill a B operand with no register moves.  Column n of
+// product block c is pair 4 n + c: the lane of column n needs positions 8 n .. 8 n + 7
+// of its four tokens, eight codes that are one contiguous 24-bit (turbo3) / 16-bit
+// (turbo2) field of each token's packed block.  Each wave parks its 16 tokens'
+// packed codes in a small LDS tile (a 48-byte row per token) and every lane reads
+// its four fields from it and looks the code pairs up: 16 lookups and 8 products per
+// unit for up to four heads, 16 products for eight.
+// The weights are written to a small LDS tile, as packed (hi, lo) fp16 pairs, by the
+// lanes that computed them (two (head, token) pairs each) and read back into the A
+// layout by byte permutes.  The softmax runs once per
 // batch of four units (64 rows): one running-max update, one sum and one wave
 // barrier for the batch's tiles.  w = exp(s - m) n 2^(15 - E), with E the exponent of
 // the largest value norm seen so far, lies below 2^15, inside fp16's range, and keeps
@@ -1014,17 +1064,21 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 // exp(m_old - m_new).
 
 constexpr int kAttnDepth = 4;          // 16-row units in flight per wave
-constexpr int kAttnGroupsPerCu = 2;    // the target of the row chunking
+// Workgroups per CU: LDS (41 KB turbo3, 62 KB turbo2) and VGPRs allow three turbo3
+// groups, two turbo2; also the target of the row chunking.
+constexpr int attn_groups_per_cu(int bits) { return bits == 3 ? 3 : 2; }
 constexpr int kAttnRaw = 16 * 48;      // bytes of a wave's packed-code tile (16 rows)
 constexpr int kAttnRec = 4 + kBlock;   // workspace floats per partial: m, l, -, -, acc[128]
 constexpr int kAttnWExp = 15;          // the weights' power-of-two headroom below fp16's max
 
-// Value lookup table: entry e (two codes, the first in the low bits) -> the dwords
-// (yh0 | yl0 << 16, yh1 | yl1 << 16), kLdsCopies8 copies.
-constexpr int attn_vtable_bytes(int bits) { return (1 << (2 * bits)) * kLdsCopies8 * 8; }
+// Value lookups: entry e (two codes, the first in the low bits) -> the dwords
+// (yh0 | yh1 << 16, yl0 | yl1 << 16), kLdsCopies8 copies: for turbo3 the q.K table
+// itself, for turbo2 a table of its own (the q.K entries there hold four codes).
+constexpr int attn_vtable_bytes(int bits) { return bits == 3 ? 0 : 16 * kLdsCopies8 * 8; }
 
-template <int BITS>
-__global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
+// NHS: sets of four query heads per pass (1: up to four heads, 2: up to eight).
+template <int BITS, int NHS>
+__global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_kernel(
     const uint8_t *__restrict__ k_codes, const uint16_t *__restrict__ k_norms,
     const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
     const uint16_t *__restrict__ q, float *__restrict__ work, uint32_t Hkv, int64_t Tc,
@@ -1034,21 +1088,23 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
     constexpr int NC = QkTable<BITS>::NC, EB = QkTable<BITS>::EB;
     constexpr int CB = 16 * BITS;   // code bytes per block
     constexpr int LW = BITS;        // code words per lane (32 codes)
-    constexpr int VNE = 1 << (2 * BITS);
+    // LDS: the tables; per unit in flight the packed value codes of its 16 rows (48-byte
+    // rows, one spare dword read past the last field) and the weights [head][row] as
+    // (hi, lo); after the last unit the same bytes hold the four waves' states
     constexpr int kTables = qk_table_bytes(BITS) + attn_vtable_bytes(BITS);
-    constexpr int kMerge = kWavesPerGroup * kQkHeads * (kBlock + 2) * 4;   // after the rows
-    static_assert(kMerge <= kTables, "the merge reuses the tables' bytes");
-    // the K and V tables, then (after the last unit) the four waves' states
-    __shared__ __attribute__((aligned(16))) uint8_t tables[kTables];
+    constexpr int kRawWords = kAttnRaw / 4 + 4;
+    constexpr int kRawBytes = kAttnDepth * kWavesPerGroup * kRawWords * 4;
+    constexpr int kPtBytes = kAttnDepth * kWavesPerGroup * kQkHeads * 16 * 4;
+    constexpr int kMerge = kWavesPerGroup * kQkHeads * kAttnRec * 4;
+    static_assert(kMerge <= kTables + kRawBytes + kPtBytes, "the merge reuses the tiles' bytes");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kTables + kRawBytes + kPtBytes];
     __shared__ __attribute__((aligned(16))) _Float16 qa[16 * kBlock];
-    // per unit in flight: the packed value codes of its 16 rows (48-byte rows, one
-    // spare dword read past the last field) and the weights [head][row]
-    __shared__ __attribute__((aligned(16))) uint32_t raw[kAttnDepth][kWavesPerGroup][kAttnRaw / 4 + 4];
-    __shared__ __attribute__((aligned(16))) float ptile[kAttnDepth][kWavesPerGroup][kQkHeads * 16];
     __shared__ __attribute__((aligned(16))) float ftile[kWavesPerGroup][kQkHeads];
     __shared__ float pw_s[kQkHeads];
     __shared__ float lv[8];
-    uint8_t *ktable = tables, *vtable = tables + qk_table_bytes(BITS);
+    uint8_t *ktable = smem, *vtable = BITS == 3 ? smem : smem + qk_table_bytes(BITS);
+    uint32_t *raw_base = (uint32_t *)(smem + kTables);
+    uint32_t *pt_base = (uint32_t *)(smem + kTables + kRawBytes);
 
     const uint32_t pass = blockIdx.x % passes;
     const uint32_t bg = blockIdx.x / passes;           // b * Hkv + g
@@ -1070,12 +1126,14 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
     const uint32_t nunits = first < last ? (last - first + 15u) / 16u : 0u;
 
     // K and V codes of this lane's run (row n, values 32 part ..) of unit k, and a
-    // batch's norms (row first + 16 k + lane, one per lane: kAttnDepth units = 64 rows);
-    // loads unconditional as in qk_kernel (rows past the wave's range read valid rows
-    // and are never used)
+    // batch's norms (row first + 16 k + lane, one per lane: kAttnDepth units = 64 rows).
+    // Rows past the wave's range are clamped to its last row (a wave without rows: the
+    // chunk's last), so the loads are unconditional, stay in bounds and re-read lines
+    // the wave has just fetched; their values are never used.
+    const uint32_t lastc = nunits ? last - 1u : t_end - 1u;
     auto fetch = [&](uint32_t k, uint32_t (&wk)[LW], uint32_t (&wv)[LW]) {
-        const uint32_t tb = min(first + k * 16u, t_end - 1u);
-        const uint32_t r = min(n, t_end - 1u - tb);
+        const uint32_t tb = min(first + k * 16u, lastc);
+        const uint32_t r = min(n, lastc - tb);
         const size_t off = (row0 + tb) * CB + (__umul24(r, (uint32_t)CB) + part * (4 * BITS));
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
@@ -1084,29 +1142,32 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
         }
     };
     static_assert(kAttnDepth * 16 == 64, "one norm load per lane per batch");
-    static_assert(kAttnDepth % 2 == 0, "tiles alternate between units");
     auto fetch_norms = [&](uint32_t k, uint32_t &nk, uint32_t &nv) {
-        const uint32_t t = min(first + 16u * k + lane, t_end - 1u);
+        const uint32_t t = min(first + 16u * k + lane, lastc);
         nk = ld_stream(k_norms + row0 + t);
         nv = ld_stream(v_norms + row0 + t);
     };
-    uint32_t wkn[kAttnDepth][LW], wvn[kAttnDepth][LW];
-    uint32_t nkn = 0, nvn = 0;
+    // a batch's codes and norms; each unit's registers are refilled with the next
+    // batch's unit as soon as they have been consumed
+    uint32_t wk[kAttnDepth][LW], wv[kAttnDepth][LW];
+    uint32_t nkc = 0, nvc = 0;
+    fetch_norms(0, nkc, nvc);   // norms first, as in the loop
 #pragma unroll
     for (int d = 0; d < kAttnDepth; ++d)
-        fetch(d, wkn[d], wvn[d]);
-    fetch_norms(0, nkn, nvn);
+        fetch(d, wk[d], wv[d]);
 
     // tables and query operands
     levels_to_lds(lv, cb);
     __syncthreads();
     qk_fill_table<BITS>(ktable, lv);
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(VNE * kLdsCopies8); i += blockDim.x) {
-        const uint32_t e = i / kLdsCopies8;
-        _Float16 a0, c0, a1, c1;
-        split_f16(lv[e & ((1u << BITS) - 1u)], a0, c0);
-        split_f16(lv[e >> BITS], a1, c1);
-        *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, c0), pack_h2(a1, c1)};
+    if constexpr (BITS == 2) {
+        for (uint32_t i = threadIdx.x; i < 16u * kLdsCopies8; i += blockDim.x) {
+            const uint32_t e = i / kLdsCopies8;
+            _Float16 a0, c0, a1, c1;
+            split_f16(lv[e & 3u], a0, c0);
+            split_f16(lv[e >> 2], a1, c1);
+            *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
+        }
     }
     qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale);
     __syncthreads();
@@ -1131,49 +1192,36 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
     // 8 n .. 8 n + 7): dwords dA, dA + 1 of the row, shifted by fsh
     constexpr int FBITS = 8 * BITS;
     const uint32_t dA = (FBITS * n) >> 5, fsh = (FBITS * n) & 31u;
+    // A rows: lane n of a lane group is row n = 8 hilo + 2 hh + e.  A token's four
+    // k-slots take (yh of parity 0, yh of parity 1, yl of parity 0, yl of parity 1), so
+    // its two A dwords are both (w, 0) for parity 0 and (0, w) for parity 1, w the hi or
+    // lo half of the packed weight: one byte permute
+    const uint32_t a_hh = (n >> 1) & 3u;
+    const uint32_t sel_w = (n & 8u) ? 0x0C0C0302u : 0x0C0C0100u;
+    const uint32_t a_sel = (n & 1u) ? ((sel_w << 16) | 0x0C0Cu) : sel_w;
+    // after the hi/lo combine, lane l holds head hv of each set: rows 4 (l / 16) .. + 3
+    // are heads 2 ((l / 16) & 1) and + 1, each at both parities
+    const uint32_t hv = 2u * (part & 1u) + (lane >> 5);
 
     // online softmax state: running max and sum of heads hu, hu + 2 (the same in all 16
     // lanes of a row), the value-norm exponent E (wave-wide) and the P.V accumulators
-    // (rows 4 (lane / 16) .. + 3 = heads hi / lo, column lane % 16 of value block c)
+    // (head set s, product block c: rows 4 (lane / 16) .. + 3, column lane % 16)
     float m_u = -__builtin_inff(), m_v = -__builtin_inff(), l_u = 0.0f, l_v = 0.0f;
     int E = -1000;
-    f4_t acc[8];
+    f4_t acc[NHS][4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        acc[c] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hs = 0; hs < NHS; ++hs)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            acc[hs][c] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // max / sum over the 16 lanes of a row (one token each)
-    auto row_max = [](float x) {
-        x = __builtin_fmaxf(x, dpp_f32<0xB1>(x));
-        x = __builtin_fmaxf(x, dpp_f32<0x4E>(x));
-        x = __builtin_fmaxf(x, dpp_f32<0x124>(x));   // row_ror:4
-        x = __builtin_fmaxf(x, dpp_f32<0x128>(x));   // row_ror:8
-        return x;
-    };
-    auto row_sum = [](float x) {
-        x += dpp_f32<0xB1>(x);
-        x += dpp_f32<0x4E>(x);
-        x += dpp_f32<0x124>(x);
-        x += dpp_f32<0x128>(x);
-        return x;
-    };
 
+    // batches of units k0 .. k0 + kAttnDepth - 1 (unit k0 holds a live row); the next
+    // batch's norms are requested first, so that they are the oldest loads in flight
+    // when that batch starts
     for (uint32_t k0 = 0; k0 < nunits; k0 += kAttnDepth) {
-        uint32_t wkc[kAttnDepth][LW], wvc[kAttnDepth][LW];
-#pragma unroll
-        for (int d = 0; d < kAttnDepth; ++d)
-#pragma unroll
-            for (int i = 0; i < LW; ++i) {
-                wkc[d][i] = wkn[d][i];
-                wvc[d][i] = wvn[d][i];
-            }
-        const uint32_t nkc = nkn, nvc = nvn;
-        if (k0 + kAttnDepth < nunits) {
-#pragma unroll
-            for (int d = 0; d < kAttnDepth; ++d)
-                fetch(k0 + kAttnDepth + d, wkn[d], wvn[d]);
-            fetch_norms(k0 + kAttnDepth, nkn, nvn);
-        }
+        uint32_t nkn, nvn;
+        fetch_norms(k0 + kAttnDepth, nkn, nvn);
         // scores of heads hu, hu + 2 for token n of each unit (as qk_kernel), -inf past
         // the range; the units' packed value codes into their tiles (row n, bytes
         // 4 BITS part ..)
@@ -1181,11 +1229,11 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
         float bu = -__builtin_inff(), bv = -__builtin_inff(), bn = 0.0f;
 #pragma unroll
         for (int d = 0; d < kAttnDepth; ++d) {
-            uint32_t *rt = raw[d][wave];
+            uint32_t *rt = raw_base + (d * kWavesPerGroup + wave) * kRawWords;
 #pragma unroll
             for (int i = 0; i < LW; ++i)
-                rt[n * 12 + part * LW + i] = wvc[d][i];
-            const f4_t Du = qk_unit<BITS>(A, wkc[d], tcopy);
+                rt[n * 12 + part * LW + i] = wv[d][i];
+            const f4_t Du = qk_unit<BITS>(A, wk[d], tcopy);
             const uint16_t nk16 = (uint16_t)__shfl((int)nkc, 16 * d + (int)n, 64);
             const uint16_t nv16 = (uint16_t)__shfl((int)nvc, 16 * d + (int)n, 64);
             const f4_t sc = Du * (float)__builtin_bit_cast(_Float16, nk16);
@@ -1199,14 +1247,15 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
             bu = __builtin_fmaxf(bu, su[d]);
             bv = __builtin_fmaxf(bv, sv[d]);
             bn = __builtin_fmaxf(bn, live ? nvd[d] : 0.0f);
+            fetch(k0 + kAttnDepth + d, wk[d], wv[d]);
         }
         // online softmax over the batch's 64 rows (unit k0 holds a live row, so the
         // maxima are finite); the value-norm exponent follows the largest norm so far
-        const float mu = __builtin_fmaxf(m_u, row_max(bu));
-        const float mv = __builtin_fmaxf(m_v, row_max(bv));
+        const float mu = __builtin_fmaxf(m_u, row16_max(bu));
+        const float mv = __builtin_fmaxf(m_v, row16_max(bv));
         const float au = __expf(m_u - mu), av = __expf(m_v - mv);
         int eu = 0;
-        (void)frexpf(row_max(bn), &eu);
+        (void)frexpf(row16_max(bn), &eu);
         const int En = max(E, __builtin_amdgcn_readfirstlane(eu));
         float ru = 0.0f, rv = 0.0f;
 #pragma unroll
@@ -1214,12 +1263,12 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
             const float pu = __expf(su[d] - mu), pv = __expf(sv[d] - mv);
             ru += pu;
             rv += pv;
-            float *pt = ptile[d][wave];
-            pt[hu * 16 + n] = ldexpf(pu * nvd[d], kAttnWExp - En);
-            pt[(hu + 2) * 16 + n] = ldexpf(pv * nvd[d], kAttnWExp - En);
+            uint32_t *pt = pt_base + (d * kWavesPerGroup + wave) * (kQkHeads * 16);
+            pt[hu * 16 + n] = split_pack(ldexpf(pu * nvd[d], kAttnWExp - En));
+            pt[(hu + 2) * 16 + n] = split_pack(ldexpf(pv * nvd[d], kAttnWExp - En));
         }
-        l_u = l_u * au + row_sum(ru);
-        l_v = l_v * av + row_sum(rv);
+        l_u = l_u * au + row16_sum(ru);
+        l_v = l_v * av + row16_sum(rv);
         m_u = mu;
         m_v = mv;
         const bool resc = __any(au != 1.0f || av != 1.0f) || En != E;
@@ -1230,83 +1279,84 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
                 ft[hu + 2] = av * sE;
             }
             wave_lds_sync();
-            const float4 f4 = *(const float4 *)(ft + 4 * (part & 1u));
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                acc[c] = acc[c] * f4_t{f4.x, f4.y, f4.z, f4.w};
+            for (int hs = 0; hs < NHS; ++hs) {
+                const float2 f2 = *(const float2 *)(ft + 4 * hs + 2 * (part & 1u));
+                const f4_t f4 = f4_t{f2.x, f2.x, f2.y, f2.y};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[hs][c] = acc[hs][c] * f4;
+            }
         }
         E = En;
         wave_lds_sync();   // weights and code tiles complete
 #pragma unroll
         for (int d = 0; d < kAttnDepth; ++d) {
-            const uint32_t *rt = raw[d][wave];
-            const float *pt = ptile[d][wave];
-            // A: row lane % 16 = head (lane % 8), hi (rows 0..7) or lo (8..15) part of
-            // the weights of tokens 4 (lane / 16) .. + 3, each twice (for yh and yl)
-            h8_t Ap;
-            {
-                const float4 x = *(const float4 *)(pt + (n & 7u) * 16 + 4 * part);
-                const float xv[4] = {x.x, x.y, x.z, x.w};
-                uint32_t hw[4];
+            const uint32_t *rt = raw_base + (d * kWavesPerGroup + wave) * kRawWords;
+            const uint32_t *pt = pt_base + (d * kWavesPerGroup + wave) * (kQkHeads * 16);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    _Float16 hi, lo;
-                    split_f16(xv[k], hi, lo);
-                    const _Float16 sel = n < 8 ? hi : lo;
-                    hw[k] = pack_h2(sel, sel);
+            for (int kb = 0; kb < 2; ++kb) {
+                // B: positions 8 n + 2 c, + 1 of tokens 8 kb + 2 part, + 1 (one lookup each)
+                uint64_t ent[2][4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t *row = rt + (8 * kb + 2 * part + j) * 12 + dA;
+                    const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t e = __builtin_amdgcn_ubfe(f, 2 * BITS * c, 2 * BITS);
+                        ent[j][c] = lds_load<uint64_t>(lshl_add<8>(e, vcopy));
+                    }
                 }
-                Ap = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], hw[2], hw[3]});
-            }
-            // B: values 8 n + c of tokens 4 (lane / 16) .. + 3, two values per lookup
-            uint64_t ent[4][4];   // [token][pair j]: values 8 n + 2 j, 8 n + 2 j + 1
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t *row = rt + (4 * part + k) * 12 + dA;
-                const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
+                for (int hs = 0; hs < NHS; ++hs) {
+                    // A: the weights of head 4 hs + a_hh, tokens 8 kb + 2 part, + 1
+                    const uint2 x = *(const uint2 *)(pt + (4 * hs + a_hh) * 16 + 8 * kb + 2 * part);
+                    const uint32_t a0 = __builtin_amdgcn_perm(x.x, x.x, a_sel);
+                    const uint32_t a1 = __builtin_amdgcn_perm(x.y, x.y, a_sel);
+                    const u4_t av = u4_t{a0, a0, a1, a1};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t e = __builtin_amdgcn_ubfe(f, 2 * BITS * j, 2 * BITS);
-                    ent[k][j] = lds_load<uint64_t>(lshl_add<8>(e, vcopy));
+                    for (int c = 0; c < 4; ++c) {
+                        const u4_t bv = u4_t{(uint32_t)ent[0][c], (uint32_t)(ent[0][c] >> 32),
+                                             (uint32_t)ent[1][c], (uint32_t)(ent[1][c] >> 32)};
+                        acc[hs][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(h8_t, av), __builtin_bit_cast(h8_t, bv), acc[hs][c],
+                            0, 0, 0);
+                    }
                 }
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int j = c >> 1, sh = 32 * (c & 1);
-                const u4_t bv = u4_t{(uint32_t)(ent[0][j] >> sh), (uint32_t)(ent[1][j] >> sh),
-                                     (uint32_t)(ent[2][j] >> sh), (uint32_t)(ent[3][j] >> sh)};
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap, __builtin_bit_cast(h8_t, bv),
-                                                                acc[c], 0, 0, 0);
             }
         }
+        nkc = nkn;
+        nvc = nvn;
     }
 
-    // this wave's state: rows h (hi) and 8 + h (lo) of acc sit in lanes l and l + 32;
-    // value 8 n + c of heads hu, hu + 2; into LDS (over the tables), then merged
+    // this wave's state into LDS (over the tables), then merged: rows r (hi) and r + 8
+    // (lo) of acc sit in lanes l and l + 32; after the combine lane l holds positions
+    // 8 n .. 8 n + 7 of head 4 s + hv
     __syncthreads();   // every wave is done with the tables
-    float *mg = (float *)tables;   // [wave][head][2 + 128]
-    {
-        float ou[8], ov[8];
+    float *mg = (float *)smem;   // [wave][head][acc[128], m, l, -, -]
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float a0 = acc[c][0], a1 = acc[c][1], a2 = acc[c][2], a3 = acc[c][3];
-            swap32(a0, a1);
-            swap32(a2, a3);
-            ou[c] = ldexpf(a0 + a1, E - kAttnWExp);
-            ov[c] = ldexpf(a2 + a3, E - kAttnWExp);
-        }
-        float *ru = mg + (wave * kQkHeads + hu) * (kBlock + 2);
-        float *rv = mg + (wave * kQkHeads + hu + 2) * (kBlock + 2);
+    for (int hs = 0; hs < NHS; ++hs) {
+        float o[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            ru[2 + 8 * n + c] = ou[c];
-            rv[2 + 8 * n + c] = ov[c];
+        for (int c = 0; c < 4; ++c) {
+            float a0 = acc[hs][c][0], a1 = acc[hs][c][1], a2 = acc[hs][c][2], a3 = acc[hs][c][3];
+            swap32(a0, a2);
+            swap32(a1, a3);
+            o[2 * c] = ldexpf(a0 + a2, E - kAttnWExp);
+            o[2 * c + 1] = ldexpf(a1 + a3, E - kAttnWExp);
         }
-        if (n == 0) {
-            ru[0] = m_u;
-            ru[1] = l_u;
-            rv[0] = m_v;
-            rv[1] = l_v;
-        }
+        float *r = mg + (wave * kQkHeads + 4 * hs + hv) * kAttnRec + 8 * n;
+        *(float4 *)r = float4{o[0], o[1], o[2], o[3]};
+        *(float4 *)(r + 4) = float4{o[4], o[5], o[6], o[7]};
+    }
+    if (n == 0) {
+        float *ru = mg + (wave * kQkHeads + hu) * kAttnRec + kBlock;
+        float *rv = mg + (wave * kQkHeads + hu + 2) * kAttnRec + kBlock;
+        ru[0] = m_u;
+        ru[1] = l_u;
+        rv[0] = m_v;
+        rv[1] = l_v;
     }
     __syncthreads();
     {
@@ -1315,16 +1365,18 @@ __global__ __launch_bounds__(256, kAttnGroupsPerCu) void attn_partial_kernel(
         float M = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w)
-            M = __builtin_fmaxf(M, mg[(w * kQkHeads + h) * (kBlock + 2)]);
+            M = __builtin_fmaxf(M, mg[(w * kQkHeads + h) * kAttnRec + kBlock]);
         float L = 0.0f, a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) {
-            const float *r = mg + (w * kQkHeads + h) * (kBlock + 2);
-            const float f = r[0] == -__builtin_inff() ? 0.0f : __expf(r[0] - M);
-            L += f * r[1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] += f * r[2 + v0 + i];
+            const float *r = mg + (w * kQkHeads + h) * kAttnRec;
+            const float f = r[kBlock] == -__builtin_inff() ? 0.0f : __expf(r[kBlock] - M);
+            L += f * r[kBlock + 1];
+            const float4 x = *(const float4 *)(r + v0);
+            a[0] += f * x.x;
+            a[1] += f * x.y;
+            a[2] += f * x.z;
+            a[3] += f * x.w;
         }
         if (h < nh) {
             float *rec = work + (((size_t)b * Hq + h0 + h) * nparts + blockIdx.y) * kAttnRec;
@@ -1515,22 +1567,23 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
 
 
 // Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
-// device): about kAttnGroupsPerCu workgroups per CU of a 256-CU MI355X, whole batches of
-// kAttnDepth units per wave, at most 65535 chunks.
-int64_t attn_chunk_rows(int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+// device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
+// of kAttnDepth units per wave, at most 65535 chunks.
+int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
     const int64_t step = (int64_t)kWavesPerGroup * 16 * kAttnDepth;
-    const int64_t round = 256 * kAttnGroupsPerCu;
+    const int64_t round = 256 * attn_groups_per_cu(bits);
     int64_t rows = (T * B * Hkv * passes + round - 1) / round;
     rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
     rows = ((rows + step - 1) / step) * step;
     return rows < step ? step : rows;
 }
 
-int64_t attn_workspace_bytes(int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
 {
-    const int64_t chunks = (T + attn_chunk_rows(B, Hkv, T, Hq) - 1) / attn_chunk_rows(B, Hkv, T, Hq);
+    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq);
+    const int64_t chunks = (T + rows - 1) / rows;
     return B * Hq * chunks * kAttnRec * (int64_t)sizeof(float);
 }
 
@@ -1541,22 +1594,24 @@ int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
-    const int64_t rows = attn_chunk_rows(B, Hkv, T, Hq);
+    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq);
     const int64_t chunks = (T + rows - 1) / rows;
     const uint32_t nparts = (uint32_t)chunks;
     dim3 grid((uint32_t)(B * Hkv * passes), (uint32_t)chunks), block(256);
     if (bits == 3)
-        hipLaunchKernelGGL(attn_partial_kernel<3>, grid, block, 0, s, (const uint8_t *)k_codes,
-                           (const uint16_t *)k_norms, (const uint8_t *)v_codes,
-                           (const uint16_t *)v_norms, (const uint16_t *)q, (float *)work,
-                           (uint32_t)Hkv, Tc, (uint32_t)T, (uint32_t)G, (uint32_t)Hq,
-                           (uint32_t)passes, (uint32_t)rows, nparts, scale, *cb);
+        hipLaunchKernelGGL((G > 4 ? attn_partial_kernel<3, 2> : attn_partial_kernel<3, 1>), grid,
+                           block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
+                           (const uint8_t *)v_codes, (const uint16_t *)v_norms,
+                           (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
+                           (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
+                           scale, *cb);
     else
-        hipLaunchKernelGGL(attn_partial_kernel<2>, grid, block, 0, s, (const uint8_t *)k_codes,
-                           (const uint16_t *)k_norms, (const uint8_t *)v_codes,
-                           (const uint16_t *)v_norms, (const uint16_t *)q, (float *)work,
-                           (uint32_t)Hkv, Tc, (uint32_t)T, (uint32_t)G, (uint32_t)Hq,
-                           (uint32_t)passes, (uint32_t)rows, nparts, scale, *cb);
+        hipLaunchKernelGGL((G > 4 ? attn_partial_kernel<2, 2> : attn_partial_kernel<2, 1>), grid,
+                           block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
+                           (const uint8_t *)v_codes, (const uint16_t *)v_norms,
+                           (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
+                           (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
+                           scale, *cb);
     int e = (int)hipGetLastError();
     if (e)
         return e;
