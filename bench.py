@@ -23,10 +23,11 @@ step (GB/s); the dominant kernel's roofline is timed with HIP events on the
 launch stream over the same timed steps; cpu_baseline times the CPU oracle on
 whole steps of the same inputs (at least 10 s of CPU work).  Outside the timed
 steps and not part of value: "decode_step" times the read path at the decode-step
-size (16 sequences, each a turbo3 K cache [8 kv heads, 32768 rows, 128] prefilled
-by encode, the 1-token append of K and V at row 32767, then q.K of 32 query heads
-over all rows); "bandwidth_configs" times encode and decode of a whole 14B-shaped
-turbo3 cache and a head_dim-256 turbo2 cache.
+size (16 sequences, each with turbo3 K and V caches [8 kv heads, 32768 rows, 128]
+prefilled by encode: the 1-token append of K and V at row 32767, q.K of 32 query
+heads over all rows, and the fused decode attention of the 32 heads over the
+compressed K and V); "bandwidth_configs" times encode and decode of a whole
+14B-shaped turbo3 cache and a head_dim-256 turbo2 cache.
 """
 from __future__ import annotations
 
@@ -56,6 +57,12 @@ def codec_bytes(nblocks: int, bits: int) -> int:
 
 def qk_bytes(B, Hkv, T_, m, Hq, bits) -> int:
     return B * Hkv * T_ * m * (16 * bits + 2) + B * Hq * T_ * 4 + B * Hq * m * 128 * 2
+
+
+def attn_bytes(B, Hkv, T_, Hq, bits) -> int:
+    """Algorithmic bytes of a decode attention over T_ rows (head_dim 128): the K and V
+    codes and norms once, the fp16 queries and the fp32 outputs."""
+    return 2 * B * Hkv * T_ * (16 * bits + 2) + B * Hq * 128 * (2 + 4)
 
 
 def parse():
@@ -259,19 +266,21 @@ def measured_traffic(kernel: str):
 
 
 def decode_step(tq, gen, dev, stream, reps=20):
-    """Average times of the decode-step read path: per sequence a turbo3 K cache of
-    [8, 32768, 128] (16 sequences), rows 0..32766 prefilled by tq_encode; the 1-token
-    append of K and of V at row 32767 (two launches), and q.K of 32 query heads."""
+    """Average times of the decode-step read path: per sequence turbo3 K and V caches
+    of [8, 32768, 128] (16 sequences), rows 0..32766 prefilled by tq_encode; the 1-token
+    append of K and of V at row 32767 (two launches), q.K of 32 query heads, and the
+    fused decode attention of the 32 heads over all 32768 rows (partials + combine)."""
     import torch
     w = gen.WORKLOADS["decode_step"]
     B, Hkv, T_, D_, Hq = w.L, w.H, w.T, w.D, w.Hq
     bits = 3
     kc, kn = tq.empty_cache(bits, B, Hkv, T_, D_, dev)
     vc, vn = tq.empty_cache(bits, B, Hkv, T_, D_, dev)
-    for b in range(B):   # prefill one sequence at a time (67 MB of fp16 each)
-        xb = gen.kv_layer(w.seed, "K", w.spec, b, Hkv, T_ - 1, D_, device=dev, T_total=T_)
-        tq.tq_encode(bits, xb.unsqueeze(0), kc[b:b + 1], kn[b:b + 1], 0)
-        del xb
+    for name, c_, n_ in (("K", kc, kn), ("V", vc, vn)):
+        for b in range(B):   # prefill one sequence at a time (67 MB of fp16 each)
+            xb = gen.kv_layer(w.seed, name, w.spec, b, Hkv, T_ - 1, D_, device=dev, T_total=T_)
+            tq.tq_encode(bits, xb.unsqueeze(0), c_[b:b + 1], n_[b:b + 1], 0)
+            del xb
     tok = {}
     for name in ("K", "V"):
         t_ = torch.empty((B, Hkv, 1, D_), dtype=torch.float16, device=dev)
@@ -281,10 +290,14 @@ def decode_step(tq, gen, dev, stream, reps=20):
         tok[name] = t_
     q = gen.queries(w.seed, B, Hq, D_, device=dev)
     scores = torch.empty((B, Hq, T_), dtype=torch.float32, device=dev)
+    attn = torch.empty((B, Hq, D_), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attn_workspace_bytes(bits, B, Hkv, T_, D_, T_, Hq), dtype=torch.uint8,
+                     device=dev)
     scale = 1.0 / math.sqrt(D_)
     ops = [("append_kv", lambda: (tq.tq_encode(bits, tok["K"], kc, kn, T_ - 1),
                                   tq.tq_encode(bits, tok["V"], vc, vn, T_ - 1))),
-           ("qk", lambda: tq.tq_qk_scores(bits, kc, kn, q, scale, scores))]
+           ("qk", lambda: tq.tq_qk_scores(bits, kc, kn, q, scale, scores)),
+           ("attn", lambda: tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, attn, workspace=ws))]
     # each op back to back `reps` times between two events (the queue never drains, so
     # host launch latency stays hidden), after two untimed launches
     med = {}
@@ -299,12 +312,16 @@ def decode_step(tq, gen, dev, stream, reps=20):
         torch.cuda.synchronize()
         med[name] = e0.elapsed_time(e1) * 1e3 / reps
     qb = qk_bytes(B, Hkv, T_, 1, Hq, bits)
+    ab = attn_bytes(B, Hkv, T_, Hq, bits)
     out = {"workload": f"{B} sequences x {Hkv} kv heads x {T_} rows x {D_}, {Hq} query heads, turbo3",
            "qk_us": round(med["qk"], 2), "qk_bytes": qb,
            "qk_GBps": round(qb / (med["qk"] * 1e-6) / 1e9, 1),
            "qk_frac_of_hbm_peak": round(qb / (med["qk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "attn_us": round(med["attn"], 2), "attn_bytes": ab,
+           "attn_GBps": round(ab / (med["attn"] * 1e-6) / 1e9, 1),
+           "attn_frac_of_hbm_peak": round(ab / (med["attn"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "append_kv_us": round(med["append_kv"], 2)}
-    del kc, kn, vc, vn, scores
+    del kc, kn, vc, vn, scores, attn, ws
     torch.cuda.empty_cache()
     return out
 

@@ -15,7 +15,7 @@ import torch
 import gen
 import kv_cache_quantization_block_amd as tq
 import oracle
-from _parity import check_codes, check_decode, check_norms, check_scores
+from _parity import check_attn, check_codes, check_decode, check_norms, check_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -132,10 +132,12 @@ def test_head_dim_256_turbo2():
 
 
 def test_decode_step_read_path():
-    """Decode step: per sequence a turbo3 K cache [8, 32768, 128] (16 sequences), rows
-    0..32766 prefilled by tq_encode, row 32767 appended for K and V, then the fused q.K
-    of 32 query heads (GQA 4) over all 32768 rows.  Appended rows and 16384 sampled
-    scores against the oracle; the prefilled rows are untouched by the append."""
+    """Decode step: per sequence turbo3 K and V caches [8, 32768, 128] (16 sequences),
+    rows 0..32766 prefilled by tq_encode, row 32767 appended for K and V, then the
+    fused q.K of 32 query heads (GQA 4) over all 32768 rows and the fused decode
+    attention over K and V.  Appended rows, 16384 sampled scores and the attention of
+    three sampled (sequence, kv head) pairs against the oracle; the prefilled rows are
+    untouched by the append."""
     w = gen.WORKLOADS["decode_step"]
     B, Hkv, T, D, Hq = w.L, w.H, w.T, w.D, w.Hq
     G = Hq // Hkv
@@ -193,3 +195,22 @@ def test_decode_step_read_path():
     res = check_scores(got, ref, scale * np.linalg.norm(qn, axis=1), np.linalg.norm(khat, axis=1),
                        "decode_step q.K")
     print(res)
+
+    # the fused decode attention of all heads over all rows (the launch the benchmark
+    # times); three sampled (sequence, kv head) pairs, all G of their heads, against
+    # the oracle on those caches alone
+    vc, vn = caches["V"]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    qh = q.cpu().numpy()
+    for b_, g_ in ((0, 0), (7, 5), (B - 1, Hkv - 1)):
+        sl = (slice(b_, b_ + 1), slice(g_, g_ + 1))
+        kcs, kns = kc[sl].cpu().numpy(), kn[sl].cpu().numpy()
+        vcs, vns = vc[sl].cpu().numpy(), vn[sl].cpu().numpy()
+        ref = oracle.attn_decode(bits, kcs, kns, vcs, vns, qh[b_:b_ + 1, g_ * G:(g_ + 1) * G], scale)
+        vhat = oracle.decode_blocks(bits, vcs.reshape(-1, 48), vns.reshape(-1))[0]
+        vmax = np.full((1, G), np.abs(vhat).max())
+        print(check_attn(out[b_:b_ + 1, g_ * G:(g_ + 1) * G].cpu().numpy(), ref, vmax, T,
+                         f"decode_step attention b={b_} g={g_}"))
