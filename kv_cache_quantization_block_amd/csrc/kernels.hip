@@ -1034,7 +1034,8 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 // acc = sum_t exp(s_t - m) n_t y_t; the four waves' states are merged in LDS and the
 // workgroup writes one (m, l, acc) per head to the workspace.  attn_combine_kernel:
 // one workgroup per (sequence, query head) merges the chunks, transforms acc once and
-// divides by 128 l.
+// divides by 128 l.  Scores, m and the workspace's m are kept in log2 units (the
+// query scale carries log2 e), so every exponential is one v_exp_f32.
 //
 // P.V runs on the matrix cores too: v_mfma_f32_16x16x32_f16 over the 16 rows (tokens)
 // of a unit, for a set of four query heads.  Row r = 8 hilo + 2 hh + e of A stands for
@@ -1070,6 +1071,10 @@ constexpr int attn_groups_per_cu(int bits) { return bits == 3 ? 3 : 2; }
 constexpr int kAttnRaw = 16 * 48;      // bytes of a wave's packed-code tile (16 rows)
 constexpr int kAttnRec = 4 + kBlock;   // workspace floats per partial: m, l, -, -, acc[128]
 constexpr int kAttnWExp = 15;          // the weights' power-of-two headroom below fp16's max
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// 2^x by the hardware's v_exp_f32 (2^-inf = 0).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value lookups: entry e (two codes, the first in the low bits) -> the dwords
 // (yh0 | yh1 << 16, yl0 | yl1 << 16), kLdsCopies8 copies: for turbo3 the q.K table
@@ -1132,20 +1137,24 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     // the wave has just fetched; their values are never used.
     const uint32_t lastc = nunits ? last - 1u : t_end - 1u;
     auto fetch = [&](uint32_t k, uint32_t (&wk)[LW], uint32_t (&wv)[LW]) {
-        const uint32_t tb = min(first + k * 16u, lastc);
+        const uint32_t tb = min(first + k * 16u, lastc);                 // wave-uniform
         const uint32_t r = min(n, lastc - tb);
-        const size_t off = (row0 + tb) * CB + (__umul24(r, (uint32_t)CB) + part * (4 * BITS));
+        const uint32_t lo = __umul24(r, (uint32_t)CB) + part * (4 * BITS);
+        const size_t ub = (row0 + tb) * CB;                              // wave-uniform
+        const uint32_t *kp = (const uint32_t *)(k_codes + ub + lo);
+        const uint32_t *vp = (const uint32_t *)(v_codes + ub + lo);
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
-            wk[i] = ld_stream((const uint32_t *)(k_codes + off) + i);
-            wv[i] = ld_stream((const uint32_t *)(v_codes + off) + i);
+            wk[i] = ld_stream(kp + i);
+            wv[i] = ld_stream(vp + i);
         }
     };
     static_assert(kAttnDepth * 16 == 64, "one norm load per lane per batch");
     auto fetch_norms = [&](uint32_t k, uint32_t &nk, uint32_t &nv) {
-        const uint32_t t = min(first + 16u * k + lane, lastc);
-        nk = ld_stream(k_norms + row0 + t);
-        nv = ld_stream(v_norms + row0 + t);
+        const uint32_t tb = min(first + 16u * k, lastc);                 // wave-uniform
+        const uint32_t r = min(lane, lastc - tb);
+        nk = ld_stream(k_norms + (row0 + tb) + r);
+        nv = ld_stream(v_norms + (row0 + tb) + r);
     };
     // a batch's codes and norms; each unit's registers are refilled with the next
     // batch's unit as soon as they have been consumed
@@ -1186,7 +1195,8 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     const uint32_t vcopy = (uint32_t)(uintptr_t)(lds_u8 *)vtable + (lane % kLdsCopies8) * 8;
     // after the hi/lo combine, lane l holds heads hu and hu + 2 of token l % 16
     const uint32_t hu = 4u * (part & 1u) + (lane >> 5);
-    const float pw_u = pw_s[hu], pw_v = pw_s[hu + 2];
+    // scores in log2 units, so that every exponential is a bare 2^x
+    const float pw_u = pw_s[hu] * kLog2e, pw_v = pw_s[hu + 2] * kLog2e;
     float *ft = ftile[wave];
     // this lane's 8-value field in a token row of the code tile (column n: values
     // 8 n .. 8 n + 7): dwords dA, dA + 1 of the row, shifted by fsh
@@ -1253,14 +1263,14 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
         // maxima are finite); the value-norm exponent follows the largest norm so far
         const float mu = __builtin_fmaxf(m_u, row16_max(bu));
         const float mv = __builtin_fmaxf(m_v, row16_max(bv));
-        const float au = __expf(m_u - mu), av = __expf(m_v - mv);
+        const float au = exp2_fast(m_u - mu), av = exp2_fast(m_v - mv);
         int eu = 0;
         (void)frexpf(row16_max(bn), &eu);
         const int En = max(E, __builtin_amdgcn_readfirstlane(eu));
         float ru = 0.0f, rv = 0.0f;
 #pragma unroll
         for (int d = 0; d < kAttnDepth; ++d) {
-            const float pu = __expf(su[d] - mu), pv = __expf(sv[d] - mv);
+            const float pu = exp2_fast(su[d] - mu), pv = exp2_fast(sv[d] - mv);
             ru += pu;
             rv += pv;
             uint32_t *pt = pt_base + (d * kWavesPerGroup + wave) * (kQkHeads * 16);
@@ -1370,7 +1380,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) {
             const float *r = mg + (w * kQkHeads + h) * kAttnRec;
-            const float f = r[kBlock] == -__builtin_inff() ? 0.0f : __expf(r[kBlock] - M);
+            const float f = r[kBlock] == -__builtin_inff() ? 0.0f : exp2_fast(r[kBlock] - M);
             L += f * r[kBlock + 1];
             const float4 x = *(const float4 *)(r + v0);
             a[0] += f * x.x;
@@ -1412,7 +1422,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
 #pragma unroll 4
     for (uint32_t p = wave; p < nparts; p += kWavesPerGroup) {
         const float *r = rec + (size_t)p * kAttnRec;
-        const float w = __expf(r[0] - M);   // every chunk holds a row: r[0] is finite
+        const float w = exp2_fast(r[0] - M);   // every chunk holds a row: r[0] is finite
         L += w * r[1];
         a += w * r[4 + lane];
         c += w * r[68 + lane];
