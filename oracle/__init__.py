@@ -57,18 +57,18 @@ def _load():
     lib.tqo_fwht128.restype = None
     lib.tqo_fwht128.argtypes = [vp]
     lib.tqo_encode_blocks.restype = i32
-    lib.tqo_encode_blocks.argtypes = [i32, vp, i64, vp, vp, vp, i32]
+    lib.tqo_encode_blocks.argtypes = [i32, vp, i64, vp, vp, vp, vp, i32]
     lib.tqo_decode_blocks.restype = i32
-    lib.tqo_decode_blocks.argtypes = [i32, vp, vp, i64, vp, vp, i32]
+    lib.tqo_decode_blocks.argtypes = [i32, vp, vp, i64, vp, vp, vp, i32]
     lib.tqo_encode.restype = i32
-    lib.tqo_encode.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, i32]
+    lib.tqo_encode.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp, i32]
     lib.tqo_decode.restype = i32
-    lib.tqo_decode.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i32]
+    lib.tqo_decode.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp, i32]
     lib.tqo_qk.restype = i32
-    lib.tqo_qk.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl, vp, i32]
+    lib.tqo_qk.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl, vp, vp, i32]
     lib.tqo_attn_decode.restype = i32
     lib.tqo_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl,
-                                    vp, i32]
+                                    vp, vp, i32]
     _lib = lib
     return lib
 
@@ -86,6 +86,16 @@ def _c16(a):
     if a.dtype != np.float16:
         raise ValueError(f"expected float16, got {a.dtype}")
     return a
+
+
+def _signs(signs):
+    """None, or the 128 diagonal entries (+1 / -1) of the randomised rotation H D."""
+    if signs is None:
+        return None
+    d = np.ascontiguousarray(signs, dtype=np.float64).reshape(-1)
+    if d.shape != (BLOCK,) or not np.all(np.abs(d) == 1.0):
+        raise ValueError("signs must be 128 values of +1 / -1")
+    return d
 
 
 def _check_bits(bits):
@@ -128,24 +138,28 @@ def fwht128(v) -> np.ndarray:
     return v
 
 
-def encode_blocks(bits: int, x, nthreads: int | None = None, want_dist: bool = False):
-    """x: fp16 [..., 128] → (codes u8 [nb, 16*bits], norms fp16 [nb], dist f64 [nb,128] | None)."""
+def encode_blocks(bits: int, x, nthreads: int | None = None, want_dist: bool = False,
+                  signs=None):
+    """x: fp16 [..., 128] → (codes u8 [nb, 16*bits], norms fp16 [nb], dist f64 [nb,128] | None).
+    signs: None (H) or 128 values +-1 (the randomised rotation H D)."""
     _check_bits(bits)
+    d = _signs(signs)
     x = _c16(x).reshape(-1, BLOCK)
     nb = x.shape[0]
     codes = np.zeros((nb, code_bytes(bits)), np.uint8)
     norms = np.zeros(nb, np.float16)
     dist = np.zeros((nb, BLOCK), np.float64) if want_dist else None
     rc = _load().tqo_encode_blocks(bits, _ptr(x), nb, _ptr(codes), _ptr(norms), _ptr(dist),
-                                   nthreads or default_threads())
+                                   _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_encode_blocks failed")
     return codes, norms, dist
 
 
-def decode_blocks(bits: int, codes, norms, nthreads: int | None = None):
+def decode_blocks(bits: int, codes, norms, nthreads: int | None = None, signs=None):
     """codes u8 [nb, 16*bits], norms fp16 [nb] → (xhat f64 [nb,128], fp16 RNE of it)."""
     _check_bits(bits)
+    d = _signs(signs)
     codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, code_bytes(bits))
     norms = _c16(norms).reshape(-1)
     nb = codes.shape[0]
@@ -154,17 +168,18 @@ def decode_blocks(bits: int, codes, norms, nthreads: int | None = None):
     xhat = np.zeros((nb, BLOCK), np.float64)
     x16 = np.zeros((nb, BLOCK), np.float16)
     rc = _load().tqo_decode_blocks(bits, _ptr(codes), _ptr(norms), nb, _ptr(xhat), _ptr(x16),
-                                   nthreads or default_threads())
+                                   _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_decode_blocks failed")
     return xhat, x16
 
 
 def encode(bits: int, x, codes, norms, t0: int = 0, nthreads: int | None = None,
-           want_dist: bool = False):
+           want_dist: bool = False, signs=None):
     """x fp16 [L,H,T,D] → writes cache rows [t0, t0+T) of codes u8 [L,H,Tc,D/128,16*bits]
     and norms fp16 [L,H,Tc,D/128] in place.  Returns dist [L,H,T,D] (or None)."""
     _check_bits(bits)
+    d = _signs(signs)
     x = _c16(x)
     L, H, T, D = x.shape
     if D % BLOCK:
@@ -178,15 +193,16 @@ def encode(bits: int, x, codes, norms, t0: int = 0, nthreads: int | None = None,
         raise ValueError("bad norms array")
     dist = np.zeros((L, H, T, D), np.float64) if want_dist else None
     rc = _load().tqo_encode(bits, _ptr(x), L, H, T, D, _ptr(codes), _ptr(norms), Tc, t0,
-                            _ptr(dist), nthreads or default_threads())
+                            _ptr(dist), _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_encode failed")
     return dist
 
 
-def decode(bits: int, codes, norms, t0: int, T: int, nthreads: int | None = None):
+def decode(bits: int, codes, norms, t0: int, T: int, nthreads: int | None = None, signs=None):
     """Cache rows [t0, t0+T) → (xhat f64 [L,H,T,D], fp16 RNE of it)."""
     _check_bits(bits)
+    d = _signs(signs)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     norms = _c16(norms)
     L, H, Tc, m, cb = codes.shape
@@ -196,16 +212,17 @@ def decode(bits: int, codes, norms, t0: int, T: int, nthreads: int | None = None
     xhat = np.zeros((L, H, T, D), np.float64)
     x16 = np.zeros((L, H, T, D), np.float16)
     rc = _load().tqo_decode(bits, _ptr(codes), _ptr(norms), L, H, Tc, D, t0, T, _ptr(xhat),
-                            _ptr(x16), nthreads or default_threads())
+                            _ptr(x16), _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_decode failed")
     return xhat, x16
 
 
 def qk_scores(bits: int, k_codes, k_norms, q, scale: float, T: int | None = None,
-              nthreads: int | None = None):
+              nthreads: int | None = None, signs=None):
     """K cache [B,Hkv,Tc,D/128,...] + q fp16 [B,Hq,D] → scores f64 [B,Hq,T]."""
     _check_bits(bits)
+    d = _signs(signs)
     k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
     k_norms = _c16(k_norms)
     q = _c16(q)
@@ -216,17 +233,18 @@ def qk_scores(bits: int, k_codes, k_norms, q, scale: float, T: int | None = None
     T = Tc if T is None else T
     scores = np.zeros((B, Hq, T), np.float64)
     rc = _load().tqo_qk(bits, _ptr(k_codes), _ptr(k_norms), B, Hkv, Tc, D, T, _ptr(q), Hq,
-                        float(scale), _ptr(scores), nthreads or default_threads())
+                        float(scale), _ptr(scores), _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_qk failed")
     return scores
 
 
 def attn_decode(bits: int, k_codes, k_norms, v_codes, v_norms, q, scale: float,
-                T: int | None = None, nthreads: int | None = None):
+                T: int | None = None, nthreads: int | None = None, signs=None):
     """K and V caches [B,Hkv,Tc,D/128,...] + q fp16 [B,Hq,D] → out f64 [B,Hq,D]:
     softmax over rows [0, T) of scale * q.k_hat, applied to v_hat."""
     _check_bits(bits)
+    d = _signs(signs)
     k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
     v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
     k_norms, v_norms, q = _c16(k_norms), _c16(v_norms), _c16(q)
@@ -239,7 +257,7 @@ def attn_decode(bits: int, k_codes, k_norms, v_codes, v_norms, q, scale: float,
     out = np.zeros((B, Hq, D), np.float64)
     rc = _load().tqo_attn_decode(bits, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
                                  B, Hkv, Tc, D, T, _ptr(q), Hq, float(scale), _ptr(out),
-                                 nthreads or default_threads())
+                                 _ptr(d), nthreads or default_threads())
     if rc:
         raise ValueError("tqo_attn_decode failed")
     return out

@@ -218,7 +218,10 @@ static void unpack_codes(int bits, const uint8_t *field, int *code)
 
 /* Encode steps, in the page's order:
  *   1. n = ||x||_2 of the 128 values (the FP16 norm the block keeps);
- *   2. rotate: u = H x;
+ *   2. rotate: u = H x, or u = H D x when a diagonal d of +-1 is given (the
+ *      randomised Hadamard rotation: TurboQuant's rotation is a random
+ *      orthogonal one, "何が違う"; H D is orthogonal up to the factor sqrt(128)
+ *      for any signs, so the norm and the normalisation are unchanged);
  *   3. normalise: t = u / n, so that sum t_i^2 = 128 (unit mean square, the
  *      scale the N(0,1) codebook expects); the unrounded norm is used, only
  *      its stored copy is rounded;
@@ -229,7 +232,7 @@ static void unpack_codes(int bits, const uint8_t *field, int *code)
  * (2^bits / 2), n16 = 0, and it decodes to exactly 0.
  * dist (optional, 128 doubles): min_k |t_i - tau_k|, for tie analysis. */
 static void encode_block(const codebook_t *cb, const uint16_t *xh, uint8_t *field,
-                         uint16_t *n16, double *dist)
+                         uint16_t *n16, double *dist, const double *d)
 {
     double x[TQO_BLOCK], u[TQO_BLOCK];
     int code[TQO_BLOCK];
@@ -242,7 +245,8 @@ static void encode_block(const codebook_t *cb, const uint16_t *xh, uint8_t *fiel
     }
     double n = sqrt(ss);
 
-    memcpy(u, x, sizeof u);
+    for (int i = 0; i < TQO_BLOCK; ++i)
+        u[i] = d ? d[i] * x[i] : x[i];
     tqo_fwht128(u);
 
     for (int i = 0; i < TQO_BLOCK; ++i) {
@@ -267,9 +271,11 @@ static void encode_block(const codebook_t *cb, const uint16_t *xh, uint8_t *fiel
 /* Decode steps: unpack, look each code up in the codebook (y_i = C[code_i]),
  * run the same transform again (v = H y) and rescale by the stored norm:
  * x_hat = (n16 / 128) * v, since H y / 128 = H^-1 y and the norm was divided
- * out before quantising.  Result kept in double (the caller may round it). */
+ * out before quantising.  With a diagonal d the inverse of H D is D H / 128,
+ * so x_hat = d * (n16 / 128) * H y.  Result kept in double (the caller may
+ * round it). */
 static void decode_block(const codebook_t *cb, const uint8_t *field, uint16_t n16,
-                         double *xhat)
+                         double *xhat, const double *d)
 {
     int code[TQO_BLOCK];
     unpack_codes(cb->bits, field, code);
@@ -278,7 +284,7 @@ static void decode_block(const codebook_t *cb, const uint8_t *field, uint16_t n1
     tqo_fwht128(xhat);
     double s = tqo_half_to_double(n16) / 128.0;
     for (int i = 0; i < TQO_BLOCK; ++i)
-        xhat[i] *= s;
+        xhat[i] *= d ? d[i] * s : s;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -334,6 +340,7 @@ typedef struct {
     uint8_t *codes;
     uint16_t *norms;
     double *dist;
+    const double *d;
 } enc_blocks_ctx;
 
 static void enc_blocks_range(void *p, int64_t lo, int64_t hi)
@@ -342,11 +349,11 @@ static void enc_blocks_range(void *p, int64_t lo, int64_t hi)
     int cbytes = 16 * c->cb.bits;
     for (int64_t b = lo; b < hi; ++b)
         encode_block(&c->cb, c->x + b * TQO_BLOCK, c->codes + b * cbytes, c->norms + b,
-                     c->dist ? c->dist + b * TQO_BLOCK : NULL);
+                     c->dist ? c->dist + b * TQO_BLOCK : NULL, c->d);
 }
 
 int tqo_encode_blocks(int bits, const uint16_t *x, int64_t nblocks, uint8_t *codes,
-                      uint16_t *norms, double *dist, int nthreads)
+                      uint16_t *norms, double *dist, const double *d, int nthreads)
 {
     enc_blocks_ctx c;
     if (get_codebook(bits, &c.cb) || nblocks < 0)
@@ -355,6 +362,7 @@ int tqo_encode_blocks(int bits, const uint16_t *x, int64_t nblocks, uint8_t *cod
     c.codes = codes;
     c.norms = norms;
     c.dist = dist;
+    c.d = d;
     parallel_for(nblocks, nthreads, enc_blocks_range, &c);
     return 0;
 }
@@ -365,6 +373,7 @@ typedef struct {
     const uint16_t *norms;
     double *xhat;
     uint16_t *x16;
+    const double *d;
 } dec_blocks_ctx;
 
 static void dec_blocks_range(void *p, int64_t lo, int64_t hi)
@@ -373,7 +382,7 @@ static void dec_blocks_range(void *p, int64_t lo, int64_t hi)
     int cbytes = 16 * c->cb.bits;
     double v[TQO_BLOCK];
     for (int64_t b = lo; b < hi; ++b) {
-        decode_block(&c->cb, c->codes + b * cbytes, c->norms[b], v);
+        decode_block(&c->cb, c->codes + b * cbytes, c->norms[b], v, c->d);
         for (int i = 0; i < TQO_BLOCK; ++i) {
             if (c->xhat)
                 c->xhat[b * TQO_BLOCK + i] = v[i];
@@ -384,7 +393,7 @@ static void dec_blocks_range(void *p, int64_t lo, int64_t hi)
 }
 
 int tqo_decode_blocks(int bits, const uint8_t *codes, const uint16_t *norms, int64_t nblocks,
-                      double *xhat, uint16_t *x16, int nthreads)
+                      double *xhat, uint16_t *x16, const double *d, int nthreads)
 {
     dec_blocks_ctx c;
     if (get_codebook(bits, &c.cb) || nblocks < 0)
@@ -393,6 +402,7 @@ int tqo_decode_blocks(int bits, const uint8_t *codes, const uint16_t *norms, int
     c.norms = norms;
     c.xhat = xhat;
     c.x16 = x16;
+    c.d = d;
     parallel_for(nblocks, nthreads, dec_blocks_range, &c);
     return 0;
 }
@@ -410,6 +420,7 @@ typedef struct {
     uint8_t *codes;
     uint16_t *norms;
     double *dist;
+    const double *d;
 } enc_ctx;
 
 /* one work item = one (l, h) pair */
@@ -424,13 +435,13 @@ static void enc_range(void *p, int64_t lo, int64_t hi)
                 int64_t src = (lh * c->T + t) * m + j;          /* block of x */
                 int64_t dst = (lh * c->Tc + c->t0 + t) * m + j; /* cache row t0 + t */
                 encode_block(&c->cb, c->x + src * TQO_BLOCK, c->codes + dst * cbytes,
-                             c->norms + dst, c->dist ? c->dist + src * TQO_BLOCK : NULL);
+                             c->norms + dst, c->dist ? c->dist + src * TQO_BLOCK : NULL, c->d);
             }
 }
 
 int tqo_encode(int bits, const uint16_t *x, int64_t L, int64_t H, int64_t T, int64_t D,
                uint8_t *codes, uint16_t *norms, int64_t Tc, int64_t t0, double *dist,
-               int nthreads)
+               const double *d, int nthreads)
 {
     enc_ctx c;
     if (get_codebook(bits, &c.cb) || D <= 0 || D % TQO_BLOCK || L < 0 || H < 0 || T < 0 ||
@@ -441,6 +452,7 @@ int tqo_encode(int bits, const uint16_t *x, int64_t L, int64_t H, int64_t T, int
     c.codes = codes;
     c.norms = norms;
     c.dist = dist;
+    c.d = d;
     parallel_for(L * H, nthreads, enc_range, &c);
     return 0;
 }
@@ -452,6 +464,7 @@ typedef struct {
     int64_t L, H, Tc, D, t0, T;
     double *xhat;
     uint16_t *x16;
+    const double *d;
 } dec_ctx;
 
 static void dec_range(void *p, int64_t lo, int64_t hi)
@@ -465,7 +478,7 @@ static void dec_range(void *p, int64_t lo, int64_t hi)
             for (int64_t j = 0; j < m; ++j) {
                 int64_t src = (lh * c->Tc + c->t0 + t) * m + j;
                 int64_t dst = (lh * c->T + t) * m + j;
-                decode_block(&c->cb, c->codes + src * cbytes, c->norms[src], v);
+                decode_block(&c->cb, c->codes + src * cbytes, c->norms[src], v, c->d);
                 for (int i = 0; i < TQO_BLOCK; ++i) {
                     if (c->xhat)
                         c->xhat[dst * TQO_BLOCK + i] = v[i];
@@ -477,7 +490,7 @@ static void dec_range(void *p, int64_t lo, int64_t hi)
 
 int tqo_decode(int bits, const uint8_t *codes, const uint16_t *norms, int64_t L, int64_t H,
                int64_t Tc, int64_t D, int64_t t0, int64_t T, double *xhat, uint16_t *x16,
-               int nthreads)
+               const double *d, int nthreads)
 {
     dec_ctx c;
     if (get_codebook(bits, &c.cb) || D <= 0 || D % TQO_BLOCK || L < 0 || H < 0 || T < 0 ||
@@ -488,6 +501,7 @@ int tqo_decode(int bits, const uint8_t *codes, const uint16_t *norms, int64_t L,
     c.L = L; c.H = H; c.Tc = Tc; c.D = D; c.t0 = t0; c.T = T;
     c.xhat = xhat;
     c.x16 = x16;
+    c.d = d;
     parallel_for(L * H, nthreads, dec_range, &c);
     return 0;
 }
@@ -510,6 +524,7 @@ typedef struct {
     const uint16_t *q;
     double scale;
     double *scores;
+    const double *d;
 } qk_ctx;
 
 static void qk_range(void *p, int64_t lo, int64_t hi)
@@ -527,7 +542,7 @@ static void qk_range(void *p, int64_t lo, int64_t hi)
         for (int64_t t = 0; t < c->T; ++t) {
             for (int64_t j = 0; j < m; ++j) {
                 int64_t blk = (bg * c->Tc + t) * m + j;
-                decode_block(&c->cb, c->codes + blk * cbytes, c->norms[blk], k + j * TQO_BLOCK);
+                decode_block(&c->cb, c->codes + blk * cbytes, c->norms[blk], k + j * TQO_BLOCK, c->d);
             }
             for (int64_t r = 0; r < G; ++r) {
                 double s = 0.0;
@@ -543,7 +558,7 @@ static void qk_range(void *p, int64_t lo, int64_t hi)
 
 int tqo_qk(int bits, const uint8_t *k_codes, const uint16_t *k_norms, int64_t B, int64_t Hkv,
            int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
-           double *scores, int nthreads)
+           double *scores, const double *d, int nthreads)
 {
     qk_ctx c;
     if (get_codebook(bits, &c.cb) || D <= 0 || D % TQO_BLOCK || B < 0 || Hkv <= 0 || Hq <= 0 ||
@@ -555,6 +570,7 @@ int tqo_qk(int bits, const uint8_t *k_codes, const uint16_t *k_norms, int64_t B,
     c.q = q;
     c.scale = scale;
     c.scores = scores;
+    c.d = d;
     parallel_for(B * Hkv, nthreads, qk_range, &c);
     return 0;
 }
@@ -576,6 +592,7 @@ typedef struct {
     const uint16_t *q;
     double scale;
     double *out;
+    const double *d;
 } attn_ctx;
 
 static void attn_range(void *p, int64_t lo, int64_t hi)
@@ -595,7 +612,7 @@ static void attn_range(void *p, int64_t lo, int64_t hi)
         for (int64_t t = 0; t < c->T; ++t) {
             for (int64_t j = 0; j < m; ++j) {
                 int64_t blk = (bg * c->Tc + t) * m + j;
-                decode_block(&c->cb, c->kc + blk * cbytes, c->kn[blk], row + j * TQO_BLOCK);
+                decode_block(&c->cb, c->kc + blk * cbytes, c->kn[blk], row + j * TQO_BLOCK, c->d);
             }
             for (int64_t r = 0; r < G; ++r) {
                 double acc = 0.0;
@@ -625,7 +642,7 @@ static void attn_range(void *p, int64_t lo, int64_t hi)
         for (int64_t t = 0; t < c->T; ++t) {
             for (int64_t j = 0; j < m; ++j) {
                 int64_t blk = (bg * c->Tc + t) * m + j;
-                decode_block(&c->cb, c->vc + blk * cbytes, c->vn[blk], row + j * TQO_BLOCK);
+                decode_block(&c->cb, c->vc + blk * cbytes, c->vn[blk], row + j * TQO_BLOCK, c->d);
             }
             for (int64_t r = 0; r < G; ++r) {
                 double w = s[r * c->T + t];
@@ -643,7 +660,7 @@ static void attn_range(void *p, int64_t lo, int64_t hi)
 int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
                     const uint8_t *v_codes, const uint16_t *v_norms, int64_t B, int64_t Hkv,
                     int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
-                    double *out, int nthreads)
+                    double *out, const double *d, int nthreads)
 {
     attn_ctx c;
     if (get_codebook(bits, &c.cb) || D <= 0 || D % TQO_BLOCK || B < 0 || Hkv <= 0 || Hq <= 0 ||
@@ -657,6 +674,7 @@ int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
     c.q = q;
     c.scale = scale;
     c.out = out;
+    c.d = d;
     parallel_for(B * Hkv, nthreads, attn_range, &c);
     return 0;
 }

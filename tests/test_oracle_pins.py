@@ -484,3 +484,122 @@ def test_attn_decode_grouping_equals_repeated_heads():
     rep = lambda z: np.repeat(z, G, axis=1)
     b = oracle.attn_decode(bits, rep(kc), rep(kn), rep(vc), rep(vn), q, 0.2, T=Tc)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- randomised rotation H D
+
+def _signs(seed):
+    return np.where(np.random.default_rng(seed).random(128) < 0.5, -1.0, 1.0)
+
+
+def test_rotation_is_orthogonal_for_any_signs():
+    """(H D)^T (H D) = 128 I for every diagonal of signs, so the norm, the unit mean
+    square of t and the decode's 1/128 are unchanged ("何が違う": any orthogonal
+    rotation spreads the energy; TurboQuant's is a random one)."""
+    for seed in range(5):
+        M = H128 @ np.diag(_signs(seed))
+        np.testing.assert_array_equal(M.T @ M, 128.0 * np.eye(128))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_rotation_all_plus_signs_is_the_plain_codec(bits):
+    """D = I gives exactly the plain transform: codes, norms, decodes, scores, attention."""
+    ones = np.ones(128)
+    x = _rng_blocks(11, 400)
+    c0, n0, _ = oracle.encode_blocks(bits, x)
+    c1, n1, _ = oracle.encode_blocks(bits, x, signs=ones)
+    assert np.array_equal(c0, c1) and np.array_equal(n0.view(np.uint16), n1.view(np.uint16))
+    assert np.array_equal(oracle.decode_blocks(bits, c0, n0)[0], oracle.decode_blocks(bits, c0, n0, signs=ones)[0])
+    (kc, kn), (vc, vn) = _attn_inputs(bits, 12, 1, 2, 6, 128, 2)[0]
+    q = _attn_inputs(bits, 12, 1, 2, 6, 128, 2)[1]
+    assert np.array_equal(oracle.qk_scores(bits, kc, kn, q, 0.1), oracle.qk_scores(bits, kc, kn, q, 0.1, signs=ones))
+    assert np.array_equal(oracle.attn_decode(bits, kc, kn, vc, vn, q, 0.1),
+                          oracle.attn_decode(bits, kc, kn, vc, vn, q, 0.1, signs=ones))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_rotation_encode_decode_brute_force(bits):
+    """Encode with signs d: t = H D x / ||x||, nearest level; decode: D H C[code] n16/128.
+    Both checked with the dense matrix H diag(d) (scipy), argmin and numpy packing."""
+    d = _signs(13)
+    M = H128 @ np.diag(d)
+    x = _rng_blocks(14, 2000)
+    codes, norms, dist = oracle.encode_blocks(bits, x, want_dist=True, signs=d)
+    lv, _, _ = oracle.codebook(bits)
+    x64 = x.astype(np.float64)
+    n = np.linalg.norm(x64, axis=1)
+    t = (x64 @ M.T) / n[:, None]
+    near = np.argmin(np.abs(t[:, :, None] - lv[None, None, :]), axis=2)
+    clear = dist > 1e-12
+    assert clear.mean() > 0.999
+    assert np.array_equal(_unpack(codes, bits)[clear], near[clear])
+    assert np.array_equal(norms.view(np.uint16), n.astype(np.float16).view(np.uint16))
+    rng = np.random.default_rng(15)
+    code = rng.integers(0, 1 << bits, (300, 128))
+    nn = rng.uniform(0.1, 500, 300).astype(np.float16)
+    xhat, x16 = oracle.decode_blocks(bits, _pack(code, bits), nn, signs=d)
+    ref = (lv[code] @ M) * (nn.astype(np.float64)[:, None] / 128.0)     # (H D)^-1 = D H / 128
+    np.testing.assert_allclose(xhat, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    assert np.array_equal(x16.view(np.uint16), xhat.astype(np.float16).view(np.uint16))
+
+
+def test_rotation_spreads_hadamard_rows_but_not_one_hots():
+    """What a seeded sign diagonal changes.  An input along a Hadamard row is the plain
+    transform's worst case: H maps it onto one coordinate (t = sqrt(128) e_k), which
+    clamps to the outermost level, and the round trip loses most of the block.  With
+    random signs the same input is spread over all coordinates and reconstructs like
+    a Gaussian block.  A one-hot input stays flat under any H D (t = +-1 everywhere),
+    so its round trip is the plain one: gain 0.756005 for turbo3."""
+    bits = 3
+    d = _signs(16)
+    rel = {}
+    for name, signs in (("plain", None), ("rot", d)):
+        x = H128[[3, 40, 77]].astype(np.float16)
+        c, n, _ = oracle.encode_blocks(bits, x, signs=signs)
+        xh, _ = oracle.decode_blocks(bits, c, n, signs=signs)
+        rel[name] = np.sum((xh - x.astype(np.float64)) ** 2, axis=1) / np.sum(x.astype(np.float64) ** 2, axis=1)
+    assert np.all(rel["plain"] > 0.5)
+    assert np.all(rel["rot"] < 0.1)
+    x = np.zeros((1, 128), np.float16)
+    x[0, 9] = 1.0
+    c, n, _ = oracle.encode_blocks(bits, x, signs=d)
+    xh, _ = oracle.decode_blocks(bits, c, n, signs=d)
+    ref = np.zeros(128)
+    ref[9] = 0.75600528
+    np.testing.assert_allclose(xh[0], ref, atol=1e-7)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_rotation_qk_and_attention_against_dense(bits):
+    """Scores and attention over caches encoded with signs d, against keys and values
+    rebuilt densely as D H C[code] n16/128 and scipy's softmax."""
+    import scipy.special
+    d = _signs(17)
+    M = H128 @ np.diag(d)
+    rng = np.random.default_rng(18)
+    B, Hkv, G, Tc, T, D = 1, 2, 3, 10, 8, 256
+    m = D // 128
+    caches = []
+    for _ in range(2):
+        x = rng.standard_normal((B, Hkv, Tc, D)).astype(np.float16)
+        codes = np.zeros((B, Hkv, Tc, m, 16 * bits), np.uint8)
+        norms = np.zeros((B, Hkv, Tc, m), np.float16)
+        oracle.encode(bits, x, codes, norms, signs=d)
+        caches.append((codes, norms))
+    (kc, kn), (vc, vn) = caches
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float16)
+    scale = 0.2
+    lv, _, _ = oracle.codebook(bits)
+
+    def dense(codes, norms):
+        y = lv[_unpack(codes, bits)].reshape(B, Hkv, Tc, m, 128)
+        return ((y @ M) * (norms.astype(np.float64)[..., None] / 128)).reshape(B, Hkv, Tc, D)[:, :, :T]
+
+    kh, vh = dense(kc, kn), dense(vc, vn)
+    qd = q.astype(np.float64).reshape(B, Hkv, G, D)
+    s = scale * np.einsum("bgrd,bgtd->bgrt", qd, kh)
+    got = oracle.qk_scores(bits, kc, kn, q, scale, T=T, signs=d)
+    np.testing.assert_allclose(got, s.reshape(B, Hkv * G, T), rtol=1e-12, atol=1e-12 * np.abs(s).max())
+    ref = np.einsum("bgrt,bgtd->bgrd", scipy.special.softmax(s, axis=-1), vh).reshape(B, Hkv * G, D)
+    out = oracle.attn_decode(bits, kc, kn, vc, vn, q, scale, T=T, signs=d)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
