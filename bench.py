@@ -26,8 +26,9 @@ steps and not part of value: "decode_step" times the read path at the decode-ste
 size (16 sequences, each with turbo3 K and V caches [8 kv heads, 32768 rows, 128]
 prefilled by encode: the 1-token append of K and V at row 32767, q.K of 32 query
 heads over all rows, and the fused decode attention of the 32 heads over the
-compressed K and V); "bandwidth_configs" times encode and decode of a whole
-14B-shaped turbo3 cache and a head_dim-256 turbo2 cache.
+compressed K and V); "rotation" times turbo3 encode and decode of the layer with the
+randomised rotation H D (seeded signs); "bandwidth_configs" times encode and decode of
+a whole 14B-shaped turbo3 cache and a head_dim-256 turbo2 cache.
 """
 from __future__ import annotations
 
@@ -95,6 +96,7 @@ def main():
 
     import gen
     import kv_cache_quantization_block_amd as tq
+    import numpy as np
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -179,6 +181,27 @@ def main():
             per_op[name]["Gvalues_per_s"] = round(op_values[name] / (us * 1e-6) / 1e9, 2)
     dom = max(per_op, key=lambda k: per_op[k]["us"])   # the dominant kernel of the step
     dom_i = [o[0] for o in ops].index(dom)
+
+    # the randomised rotation H D (seeded signs, not part of the step): turbo3 encode and
+    # decode of the same layer through the _rot entry points, timed like the table above
+    signs = np.where(np.random.default_rng(w.seed).random(128) < 0.5, -1.0, 1.0)
+    b3 = bufs[3]
+    rotation = {}
+    for name, fn in (("encode_turbo3_rot", lambda: tq.tq_encode(3, b3["x"], *b3["c"], 0, signs=signs)),
+                     ("decode_turbo3_rot", lambda: tq.tq_decode(3, *b3["c"], 0, b3["o"], signs=signs))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = codec_bytes(nblk, 3)
+        plain = per_op[name[:-4]]["us"]
+        rotation[name] = {"us": round(us, 2), "bytes": nbytes,
+                          "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "vs_plain": round(us / plain, 3)}
     for _ in range(2):
         step()
     torch.cuda.synchronize()
@@ -233,6 +256,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": per_op,
+        "rotation": rotation,
         "decode_step": dstep,
         "bandwidth_configs": bw_cfgs,
     }

@@ -143,6 +143,36 @@ int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const voi
                    const void *q, int64_t Hq, float scale, float *out, void *workspace,
                    int64_t workspace_bytes, void *stream);
 
+/* Randomised rotation.  TurboQuant rotates each vector by a random orthogonal matrix
+ * before quantising (section "TurboQuant の何が違うのか"); the calls above use the
+ * fixed Hadamard H.  The _rot variants below use H D instead, D a diagonal of signs:
+ *   signs  host memory, 4 words (128 bits), or NULL (then exactly the call above);
+ *          bit p % 32 of signs[p / 32] set <=> D_pp = -1, for value position p of
+ *          every 128-value block.  Read during the call only.
+ * Encode rotates u = H D x; decode returns D (n16/128) H y; q.K and the attention
+ * decode the keys and values the same way (internally q' = H D q and a final D on
+ * the attention output).  A cache written with some signs must be read with the same
+ * signs.  The signs are an input: callers draw them (for instance from a seed) and
+ * keep them with the cache.  Otherwise each _rot call takes the arguments, has the
+ * layouts and returns the statuses of the call it extends.
+ * Effect: an input aligned with a row of H, which H alone collapses onto a single
+ * coordinate, is spread over all coordinates; a one-hot input stays flat under any
+ * H D (its round trip is the same as without signs). */
+int tq_encode_rot(int type, const uint32_t *signs, const void *x, int64_t L, int64_t H,
+                  int64_t T, int64_t D, void *codes, void *norms, int64_t Tc, int64_t t0,
+                  void *stream);
+int tq_decode_rot(int type, const uint32_t *signs, const void *codes, const void *norms,
+                  int64_t L, int64_t H, int64_t Tc, int64_t D, int64_t t0, int64_t T, void *x,
+                  void *stream);
+int tq_qk_scores_rot(int type, const uint32_t *signs, const void *k_codes, const void *k_norms,
+                     int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q,
+                     int64_t Hq, float scale, float *scores, void *stream);
+int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
+                       const void *k_norms, const void *v_codes, const void *v_norms, int64_t B,
+                       int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq,
+                       float scale, float *out, void *workspace, int64_t workspace_bytes,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

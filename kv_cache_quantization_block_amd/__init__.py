@@ -18,6 +18,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -80,6 +81,11 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.restype = i32
     L.tq_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp,
                                  vp, i64, vp]
+    for name, plain in (("tq_encode_rot", L.tq_encode), ("tq_decode_rot", L.tq_decode),
+                        ("tq_qk_scores_rot", L.tq_qk_scores), ("tq_attn_decode_rot", L.tq_attn_decode)):
+        f = getattr(L, name)
+        f.restype = i32
+        f.argtypes = [i32, vp] + plain.argtypes[1:]
     _lib = L
     return L
 
@@ -124,6 +130,25 @@ def tq_codebook(type: int):
 
 # ---------------------------------------------------------------- tensor calls
 
+def sign_words(signs):
+    """128 diagonal entries of the randomised rotation H D (+1 / -1, or bools where True
+    means -1) -> the four 32-bit words the _rot calls take (bit p set <=> D_pp = -1)."""
+    if isinstance(signs, torch.Tensor):
+        signs = signs.detach().cpu().numpy()
+    v = np.asarray(signs)
+    if v.shape != (128,):
+        raise ValueError("signs must hold 128 entries")
+    if v.dtype == np.bool_:
+        neg = v
+    else:
+        if not np.all(np.abs(v.astype(np.float64)) == 1.0):
+            raise ValueError("signs must be +1 / -1 (or bools)")
+        neg = v.astype(np.float64) < 0
+    w = [int(np.sum(neg[32 * k:32 * k + 32].astype(np.uint64) << np.arange(32, dtype=np.uint64)))
+         for k in range(4)]
+    return (ctypes.c_uint32 * 4)(*w)
+
+
 def _stream(stream) -> int | None:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream or None
@@ -161,35 +186,39 @@ def _cache_dims(codes: torch.Tensor, norms: torch.Tensor, type: int):
 
 
 def tq_encode(type: int, x: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
-              t0: int = 0, stream=None) -> None:
-    """Encode x [L, H, T, D] into cache rows [t0, t0 + T) (asynchronous)."""
+              t0: int = 0, stream=None, signs=None) -> None:
+    """Encode x [L, H, T, D] into cache rows [t0, t0 + T) (asynchronous).  signs: None
+    (rotation H) or the 128 signs of the randomised rotation H D (tq_encode_rot)."""
     L, H, Tc, D = _cache_dims(codes, norms, type)
     if x.dim() != 4 or tuple(x.shape[:2]) != (L, H) or x.shape[3] != D:
         raise ValueError("x must be [L, H, T, D] matching the cache")
     T = x.shape[2]
-    rc = lib().tq_encode(type, _dev(x, "x", torch.float16), L, H, T, D,
-                         _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
-                         Tc, t0, _stream(stream))
+    args = (_dev(x, "x", torch.float16), L, H, T, D, _dev(codes, "codes", torch.uint8),
+            _dev(norms, "norms", torch.float16), Tc, t0, _stream(stream))
+    rc = lib().tq_encode(type, *args) if signs is None else lib().tq_encode_rot(type, sign_words(signs), *args)
     if rc:
         raise TQError(rc, "tq_encode")
 
 
 def tq_decode(type: int, codes: torch.Tensor, norms: torch.Tensor, t0: int, x: torch.Tensor,
-              stream=None) -> None:
-    """Decode cache rows [t0, t0 + T) into x [L, H, T, D] fp16 (asynchronous)."""
+              stream=None, signs=None) -> None:
+    """Decode cache rows [t0, t0 + T) into x [L, H, T, D] fp16 (asynchronous).  signs: as
+    the cache was encoded with (tq_decode_rot), or None."""
     L, H, Tc, D = _cache_dims(codes, norms, type)
     if x.dim() != 4 or tuple(x.shape[:2]) != (L, H) or x.shape[3] != D:
         raise ValueError("x must be [L, H, T, D] matching the cache")
     T = x.shape[2]
-    rc = lib().tq_decode(type, _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
-                         L, H, Tc, D, t0, T, _dev(x, "x", torch.float16), _stream(stream))
+    args = (_dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
+            L, H, Tc, D, t0, T, _dev(x, "x", torch.float16), _stream(stream))
+    rc = lib().tq_decode(type, *args) if signs is None else lib().tq_decode_rot(type, sign_words(signs), *args)
     if rc:
         raise TQError(rc, "tq_decode")
 
 
 def tq_qk_scores(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, q: torch.Tensor,
-                 scale: float, scores: torch.Tensor, stream=None) -> None:
-    """scores [B, Hq, T] = scale * q . k_hat over key-cache rows [0, T) (asynchronous)."""
+                 scale: float, scores: torch.Tensor, stream=None, signs=None) -> None:
+    """scores [B, Hq, T] = scale * q . k_hat over key-cache rows [0, T) (asynchronous).
+    signs: as the cache was encoded with (tq_qk_scores_rot), or None."""
     B, Hkv, Tc, D = _cache_dims(k_codes, k_norms, type)
     if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
         raise ValueError("q must be [B, Hq, D] matching the cache")
@@ -197,10 +226,11 @@ def tq_qk_scores(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, q: tor
     if scores.dim() != 3 or tuple(scores.shape[:2]) != (B, Hq):
         raise ValueError("scores must be [B, Hq, T]")
     T = scores.shape[2]
-    rc = lib().tq_qk_scores(type, _dev(k_codes, "k_codes", torch.uint8),
-                            _dev(k_norms, "k_norms", torch.float16), B, Hkv, Tc, D, T,
-                            _dev(q, "q", torch.float16), Hq, float(scale),
-                            _dev(scores, "scores", torch.float32), _stream(stream))
+    args = (_dev(k_codes, "k_codes", torch.uint8), _dev(k_norms, "k_norms", torch.float16), B,
+            Hkv, Tc, D, T, _dev(q, "q", torch.float16), Hq, float(scale),
+            _dev(scores, "scores", torch.float32), _stream(stream))
+    rc = (lib().tq_qk_scores(type, *args) if signs is None
+          else lib().tq_qk_scores_rot(type, sign_words(signs), *args))
     if rc:
         raise TQError(rc, "tq_qk_scores")
 
@@ -215,10 +245,12 @@ def tq_attn_workspace_bytes(type: int, B: int, Hkv: int, Tc: int, D: int, T: int
 
 def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor,
                    v_norms: torch.Tensor, q: torch.Tensor, scale: float, out: torch.Tensor,
-                   T: int | None = None, workspace: torch.Tensor | None = None, stream=None) -> None:
+                   T: int | None = None, workspace: torch.Tensor | None = None, stream=None,
+                   signs=None) -> None:
     """out [B, Hq, D] (fp32) = softmax over rows [0, T) of scale * q . k_hat, applied to v_hat
     (asynchronous).  workspace: a uint8 device tensor of at least tq_attn_workspace_bytes;
-    when None, one is allocated here with torch (the library itself never allocates)."""
+    when None, one is allocated here with torch (the library itself never allocates).
+    signs: as the caches were encoded with (tq_attn_decode_rot), or None."""
     B, Hkv, Tc, D = _cache_dims(k_codes, k_norms, type)
     if _cache_dims(v_codes, v_norms, type) != (B, Hkv, Tc, D):
         raise ValueError("K and V caches must have the same shape")
@@ -233,13 +265,12 @@ def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_co
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
     if workspace.dtype != torch.uint8 or workspace.dim() != 1:
         raise ValueError("workspace must be a 1-d uint8 tensor")
-    rc = lib().tq_attn_decode(type, _dev(k_codes, "k_codes", torch.uint8),
-                              _dev(k_norms, "k_norms", torch.float16),
-                              _dev(v_codes, "v_codes", torch.uint8),
-                              _dev(v_norms, "v_norms", torch.float16), B, Hkv, Tc, D, T,
-                              _dev(q, "q", torch.float16), Hq, float(scale),
-                              _dev(out, "out", torch.float32),
-                              _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                              _stream(stream))
+    args = (_dev(k_codes, "k_codes", torch.uint8), _dev(k_norms, "k_norms", torch.float16),
+            _dev(v_codes, "v_codes", torch.uint8), _dev(v_norms, "v_norms", torch.float16), B, Hkv,
+            Tc, D, T, _dev(q, "q", torch.float16), Hq, float(scale),
+            _dev(out, "out", torch.float32), _dev(workspace, "workspace", torch.uint8),
+            workspace.numel(), _stream(stream))
+    rc = (lib().tq_attn_decode(type, *args) if signs is None
+          else lib().tq_attn_decode_rot(type, sign_words(signs), *args))
     if rc:
         raise TQError(rc, "tq_attn_decode")

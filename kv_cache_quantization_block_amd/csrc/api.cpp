@@ -28,6 +28,16 @@ bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t *out)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// The caller's four sign words (host memory), or none.
+tq::Signs to_signs(const uint32_t *signs)
+{
+    tq::Signs sg = {{0u, 0u, 0u, 0u}};
+    if (signs)
+        for (int k = 0; k < 4; ++k)
+            sg.w[k] = signs[k];
+    return sg;
+}
+
 // half-open byte ranges [p, p + n) overlap (empty ranges never do)
 bool overlap(const void *p, int64_t n, const void *q, int64_t m)
 {
@@ -112,8 +122,9 @@ int tq_codebook(int type, float *levels, float *thresholds)
     return TQ_OK;
 }
 
-int tq_encode(int type, const void *x, int64_t L, int64_t H, int64_t T, int64_t D, void *codes,
-              void *norms, int64_t Tc, int64_t t0, void *stream)
+int tq_encode_rot(int type, const uint32_t *signs, const void *x, int64_t L, int64_t H,
+                  int64_t T, int64_t D, void *codes, void *norms, int64_t Tc, int64_t t0,
+                  void *stream)
 {
     int64_t nblocks, cache_blocks;
     int rc = check_codec_shape(type, L, H, T, D, Tc, t0, &nblocks, &cache_blocks);
@@ -130,13 +141,21 @@ int tq_encode(int type, const void *x, int64_t L, int64_t H, int64_t T, int64_t 
         overlap(codes, cb, norms, nbytes))
         return TQ_ERR_ALIAS;
     const int64_t m = D / tq::kBlock;
-    return tq::launch_encode(type, x, nblocks, T * m, Tc * m, t0 * m, codes, norms, stream)
+    return tq::launch_encode(type, to_signs(signs), x, nblocks, T * m, Tc * m, t0 * m, codes,
+                             norms, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
 }
 
-int tq_decode(int type, const void *codes, const void *norms, int64_t L, int64_t H, int64_t Tc,
-              int64_t D, int64_t t0, int64_t T, void *x, void *stream)
+int tq_encode(int type, const void *x, int64_t L, int64_t H, int64_t T, int64_t D, void *codes,
+              void *norms, int64_t Tc, int64_t t0, void *stream)
+{
+    return tq_encode_rot(type, nullptr, x, L, H, T, D, codes, norms, Tc, t0, stream);
+}
+
+int tq_decode_rot(int type, const uint32_t *signs, const void *codes, const void *norms,
+                  int64_t L, int64_t H, int64_t Tc, int64_t D, int64_t t0, int64_t T, void *x,
+                  void *stream)
 {
     int64_t nblocks, cache_blocks;
     int rc = check_codec_shape(type, L, H, T, D, Tc, t0, &nblocks, &cache_blocks);
@@ -152,14 +171,21 @@ int tq_decode(int type, const void *codes, const void *norms, int64_t L, int64_t
     if (overlap(x, xb, codes, cb) || overlap(x, xb, norms, nbytes))
         return TQ_ERR_ALIAS;
     const int64_t m = D / tq::kBlock;
-    return tq::launch_decode(type, codes, norms, nblocks, T * m, Tc * m, t0 * m, x, stream)
+    return tq::launch_decode(type, to_signs(signs), codes, norms, nblocks, T * m, Tc * m, t0 * m,
+                             x, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
 }
 
-int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
-                 int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq, float scale,
-                 float *scores, void *stream)
+int tq_decode(int type, const void *codes, const void *norms, int64_t L, int64_t H, int64_t Tc,
+              int64_t D, int64_t t0, int64_t T, void *x, void *stream)
+{
+    return tq_decode_rot(type, nullptr, codes, norms, L, H, Tc, D, t0, T, x, stream);
+}
+
+int tq_qk_scores_rot(int type, const uint32_t *signs, const void *k_codes, const void *k_norms,
+                     int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q,
+                     int64_t Hq, float scale, float *scores, void *stream)
 {
     if (!valid_type(type))
         return TQ_ERR_TYPE;
@@ -184,9 +210,18 @@ int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, 
     if (overlap(scores, sb, k_codes, cache_blocks * 16 * type) ||
         overlap(scores, sb, k_norms, cache_blocks * 2) || overlap(scores, sb, q, qn * 2))
         return TQ_ERR_ALIAS;
-    return tq::launch_qk(type, k_codes, k_norms, B, Hkv, Tc, m, T, q, Hq, scale, scores, stream)
+    return tq::launch_qk(type, to_signs(signs), k_codes, k_norms, B, Hkv, Tc, m, T, q, Hq, scale,
+                         scores, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
+}
+
+int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
+                 int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq, float scale,
+                 float *scores, void *stream)
+{
+    return tq_qk_scores_rot(type, nullptr, k_codes, k_norms, B, Hkv, Tc, D, T, q, Hq, scale,
+                            scores, stream);
 }
 
 }  // extern "C"
@@ -221,10 +256,11 @@ int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, in
     return tq::attn_workspace_bytes(type, B, Hkv, T, Hq);
 }
 
-int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
-                   const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
-                   const void *q, int64_t Hq, float scale, float *out, void *workspace,
-                   int64_t workspace_bytes, void *stream)
+int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
+                       const void *k_norms, const void *v_codes, const void *v_norms, int64_t B,
+                       int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq,
+                       float scale, float *out, void *workspace, int64_t workspace_bytes,
+                       void *stream)
 {
     int64_t cache_blocks;
     const int st = check_attn_shape(type, B, Hkv, Tc, D, T, Hq, &cache_blocks);
@@ -249,8 +285,17 @@ int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const voi
             return TQ_ERR_ALIAS;
     if (overlap(out, ob, workspace, need))
         return TQ_ERR_ALIAS;
-    return tq::launch_attn(type, k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc, T, q, Hq, scale,
-                           out, workspace, stream)
+    return tq::launch_attn(type, to_signs(signs), k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc,
+                           T, q, Hq, scale, out, workspace, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
+}
+
+int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
+                   const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                   const void *q, int64_t Hq, float scale, float *out, void *workspace,
+                   int64_t workspace_bytes, void *stream)
+{
+    return tq_attn_decode_rot(type, nullptr, k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc, D, T,
+                              q, Hq, scale, out, workspace, workspace_bytes, stream);
 }

@@ -32,24 +32,31 @@ struct Codebook {
 // once per process, thread-safe.
 const Codebook *codebook(int bits);
 
+// Signs of the randomised rotation H D: bit p % 32 of w[p / 32] set <=> D_pp = -1
+// (all zero: the plain H).  Handed to the kernels by value.
+struct Signs {
+    uint32_t w[4];
+};
+
 // Kernel launchers (asynchronous on `stream`).  Each returns 0 on a clean
 // launch and a nonzero HIP error code otherwise.  Shapes are pre-validated.
-int launch_encode(int bits, const void *x, int64_t nblocks, int64_t row_blocks,
+int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int64_t row_blocks,
                   int64_t cache_row_blocks, int64_t t0_blocks, void *codes, void *norms,
                   void *stream);
-int launch_decode(int bits, const void *codes, const void *norms, int64_t nblocks,
-                  int64_t row_blocks, int64_t cache_row_blocks, int64_t t0_blocks, void *x,
-                  void *stream);
-int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
-              int64_t Tc, int64_t m, int64_t T, const void *q, int64_t Hq, float scale,
-              float *scores, void *stream);
+int launch_decode(int bits, const Signs &sg, const void *codes, const void *norms,
+                  int64_t nblocks, int64_t row_blocks, int64_t cache_row_blocks,
+                  int64_t t0_blocks, void *x, void *stream);
+int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norms, int64_t B,
+              int64_t Hkv, int64_t Tc, int64_t m, int64_t T, const void *q, int64_t Hq,
+              float scale, float *scores, void *stream);
 
 // Decode attention (D = 128): rows per chunk and workspace bytes follow from the sizes
 // alone; the launch runs the partial and the combine kernel.
 int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
 int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
-int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *v_codes,
-                const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t T,
-                const void *q, int64_t Hq, float scale, float *out, void *work, void *stream);
+int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_norms,
+                const void *v_codes, const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc,
+                int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
+                void *stream);
 
 }  // namespace tq

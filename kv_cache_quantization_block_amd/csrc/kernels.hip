@@ -250,6 +250,30 @@ __device__ __forceinline__ void swap32(float &a, float &b)
     b = __builtin_bit_cast(float, r1);
 }
 
+// Signs of the randomised rotation H D.  Word k of the kernel argument is read with
+// a constant index (a per-lane index would load the argument through memory).
+__device__ __forceinline__ uint32_t sign_word(const Signs &sg, uint32_t k)
+{
+    const uint32_t lo = k & 1u ? sg.w[1] : sg.w[0], hi = k & 1u ? sg.w[3] : sg.w[2];
+    return k & 2u ? hi : lo;
+}
+// fp16 sign-flip masks of the eight positions 8 c .. 8 c + 7 (one 16-byte chunk of a
+// block, as four packed pairs): XOR with them applies D to the chunk.
+__device__ __forceinline__ u4_t sign_mask_chunk(const Signs &sg, uint32_t c)
+{
+    const uint32_t byte = sign_word(sg, c >> 2) >> (8u * (c & 3u));
+    u4_t m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        m[j] = (((byte >> (2 * j)) & 1u) << 15) | (((byte >> (2 * j + 1)) & 1u) << 31);
+    return m;
+}
+// float sign-flip mask of position p < 128.
+__device__ __forceinline__ uint32_t sign_mask_f32(const Signs &sg, uint32_t p)
+{
+    return ((sign_word(sg, p >> 5) >> (p & 31u)) & 1u) << 31;
+}
+
 // Writes a finished tile: packed codes staged in LDS (block b at b * 16 * BITS)
 // and each lane's norm.  Consecutive cache blocks (always, unless the tile
 // straddles two (layer, head) rows of a cache longer than x) leave as contiguous
@@ -297,13 +321,17 @@ __device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t la
 // previous iteration), issue the loads of tile i+1, then compute tile i.  The
 // stores and the next loads are both issued before the compute, so neither the
 // load latency nor the store completions hold the wave at its next wait.
-template <int BITS>
+// ROT: rotate by H D (Signs sg) instead of H: a lane's 16-byte loads always hold the
+// same eight positions of a block (chunk lane % 16), so D is one XOR per packed pair
+// before the tile is parked in LDS.
+template <int BITS, bool ROT>
 __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restrict__ x,
                                                         uint32_t nblocks, uint32_t row_blocks,
                                                         int64_t cache_row_blocks,
                                                         int64_t t0_blocks,
                                                         uint8_t *__restrict__ codes,
-                                                        uint16_t *__restrict__ norms, Codebook cb)
+                                                        uint16_t *__restrict__ norms, Codebook cb,
+                                                        Signs sg)
 {
     constexpr int GW = BITS;              // 32-bit words per 32-code group
     constexpr int GB = 4 * BITS;          // bytes per 32-code group
@@ -324,6 +352,7 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
 
     u4_t R[8];
     load_enc_tile(R, x, tile * kEncTileBlocks, min(nblocks - tile * kEncTileBlocks, 32u), lane);
+    const u4_t smask = ROT ? sign_mask_chunk(sg, lane & 15u) : u4_t{0, 0, 0, 0};
     uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in `stage`
     uint16_t pn16 = 0;
     for (;;) {
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
         //    start loading the next one into R
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            *(u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)) = R[k];
+            *(u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)) = ROT ? R[k] ^ smask : R[k];
         wave_lds_sync();
         if (pnb)
             store_enc_tile<BITS>(stage, lane, pb0, pnb, pn16, row_blocks, cache_row_blocks,
@@ -515,32 +544,38 @@ __device__ __forceinline__ void load_codes(uint32_t (&W)[4 * BITS], uint16_t &N,
 }
 
 // Writes a decoded tile from its LDS image: 1 KB contiguous 16-byte stores.
+template <bool ROT>
 __device__ __forceinline__ void store_dec_tile(const uint8_t *lds, uint32_t lane, uint32_t b0,
-                                               uint32_t nb, uint8_t *__restrict__ x)
+                                               uint32_t nb, uint8_t *__restrict__ x, u4_t smask)
 {
     uint8_t *dst = x + (size_t)b0 * (kBlock * 2) + lane * 16;
     if (nb == kBlocksPerWave) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-            *(u4_t *)(dst + k * 1024) = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
+        for (int k = 0; k < 16; ++k) {
+            const u4_t r = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
+            *(u4_t *)(dst + k * 1024) = ROT ? r ^ smask : r;
+        }
     } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const uint32_t blk = 4 * k + (lane >> 4);
             const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
             if (blk < nb)
-                *(u4_t *)(dst + k * 1024) = r;
+                *(u4_t *)(dst + k * 1024) = ROT ? r ^ smask : r;
         }
     }
 }
 
-template <int BITS>
+// ROT: x_hat = D (n16 / 128) H y: the fp16 tile's 16-byte stores always hold the same
+// eight positions of a block (chunk lane % 16), so D is one XOR per packed pair.
+template <int BITS, bool ROT>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restrict__ codes,
                                                         const uint16_t *__restrict__ norms,
                                                         uint32_t nblocks, uint32_t row_blocks,
                                                         int64_t cache_row_blocks,
                                                         int64_t t0_blocks,
-                                                        uint8_t *__restrict__ x, Codebook cb)
+                                                        uint8_t *__restrict__ x, Codebook cb,
+                                                        Signs sg)
 {
     // Entry e (2 b code bits = two codes, the first in the low bits) -> stage-one
     // outputs (y0 + y1, y0 - y1); 64 entries for turbo3, 16 for turbo2, each
@@ -572,6 +607,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
         return;
     uint8_t *lds = smem + kTableBytes + wave * kTileBytes;
     constexpr int NW = 4 * BITS;
+    const u4_t smask = ROT ? sign_mask_chunk(sg, lane & 15u) : u4_t{0, 0, 0, 0};
 
     // Per iteration (tile i): take tile i's codes (prefetched), write out tile i-1
     // from LDS, issue the loads of tile i+1, then compute tile i into LDS.  Stores
@@ -591,7 +627,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
             w[k] = W[k];
         const float scale = (float)__builtin_bit_cast(_Float16, N) * (1.0f / 128.0f);
         if (pnb)
-            store_dec_tile(lds, lane, pb0, pnb, x);
+            store_dec_tile<ROT>(lds, lane, pb0, pnb, x, smask);
         const uint32_t next = tile + stride;
         if (next < ntiles)
             load_codes<BITS>(W, N, codes, norms, next * kBlocksPerWave + lane, nblocks,
@@ -636,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
         if (tile >= ntiles)
             break;
     }
-    store_dec_tile(lds, lane, pb0, pnb, x);
+    store_dec_tile<ROT>(lds, lane, pb0, pnb, x, smask);
 }
 
 // ---------------------------------------------------------------- q.K scores
@@ -751,17 +787,20 @@ __device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv)
 // rotates every 128-slice (lane l holds positions l and 64 + l; span 64 in-lane, spans
 // 32..1 across lanes), takes the head's largest |q'|, then writes x = q' * scale / 128 *
 // 2^(14 - e) as hi (row hh) and lo (row 8 + hh) of qa [m][16][128], and 2^(e - 14) to
-// pw_s[hh].  Heads past nh get zero rows.  The caller barriers afterwards.
+// pw_s[hh].  Heads past nh get zero rows.  The caller barriers afterwards.  With the
+// randomised rotation q' = H D q, since q . (D H y) = (H D q) . y.
 template <bool ONE_BLOCK>
 __device__ __forceinline__ void qk_prepare_queries(_Float16 *qa, float *pw_s,
                                                    const uint16_t *__restrict__ q, uint32_t b,
                                                    uint32_t Hq, uint32_t h0, uint32_t nh,
                                                    uint32_t m, uint32_t wave, uint32_t lane,
-                                                   float scale)
+                                                   float scale, const Signs &sg)
 {
+    const uint16_t fa = (uint16_t)(sign_mask_f32(sg, lane) >> 16);
+    const uint16_t fc = (uint16_t)(sign_mask_f32(sg, 64u + lane) >> 16);
     auto rotate = [&](const uint16_t *v, float &a, float &c) {
-        a = (float)__builtin_bit_cast(_Float16, v[lane]);
-        c = (float)__builtin_bit_cast(_Float16, v[64 + lane]);
+        a = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[lane] ^ fa));
+        c = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[64 + lane] ^ fc));
         const float s0 = a + c;
         c = a - c;
         a = s0;
@@ -860,7 +899,8 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                                                     float *__restrict__ scores, uint32_t Hkv,
                                                     int64_t Tc, uint32_t T, uint32_t m,
                                                     uint32_t G, uint32_t Hq, uint32_t passes,
-                                                    uint32_t tpg, float scale, Codebook cb)
+                                                    uint32_t tpg, float scale, Codebook cb,
+                                                    Signs sg)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t qk_smem[];
     constexpr int NC = QkTable<BITS>::NC;
@@ -939,7 +979,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     __syncthreads();
     qk_fill_table<BITS>(table, lv);
 
-    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale);
+    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg);
     __syncthreads();
 
     // A operands of block j for this lane's row (lane % 16) and value run
@@ -1088,7 +1128,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
     const uint16_t *__restrict__ q, float *__restrict__ work, uint32_t Hkv, int64_t Tc,
     uint32_t T, uint32_t G, uint32_t Hq, uint32_t passes, uint32_t tpg, uint32_t nparts,
-    float scale, Codebook cb)
+    float scale, Codebook cb, Signs sg)
 {
     constexpr int NC = QkTable<BITS>::NC, EB = QkTable<BITS>::EB;
     constexpr int CB = 16 * BITS;   // code bytes per block
@@ -1178,7 +1218,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
             *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         }
     }
-    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale);
+    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale, sg);
     __syncthreads();
 
     h8_t A[8];
@@ -1404,7 +1444,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
 // once and divide by 128 l.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ work,
                                                            float *__restrict__ out,
-                                                           uint32_t nparts)
+                                                           uint32_t nparts, Signs sg)
 {
     __shared__ float red[kWavesPerGroup][kBlock + 1];
     const uint32_t lane = threadIdx.x & 63u;
@@ -1448,9 +1488,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
         a = up ? pa - a : a + pa;
         c = up ? pc - c : c + pc;
     }
+    // D H acc / (128 l): the randomised rotation's signs flip the output positions
     const float inv = 1.0f / (128.0f * L);
-    out[(size_t)bh * kBlock + lane] = a * inv;
-    out[(size_t)bh * kBlock + 64 + lane] = c * inv;
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a * inv) ^ sign_mask_f32(sg, lane);
+    const uint32_t uc = __builtin_bit_cast(uint32_t, c * inv) ^ sign_mask_f32(sg, 64u + lane);
+    out[(size_t)bh * kBlock + lane] = __builtin_bit_cast(float, ua);
+    out[(size_t)bh * kBlock + 64 + lane] = __builtin_bit_cast(float, uc);
 }
 
 // Compute units of the current device (cached per device).
@@ -1493,7 +1536,9 @@ inline int grid_for(int64_t nblocks, int tile_blocks, int per_cu)
 
 }  // namespace
 
-int launch_encode(int bits, const void *x, int64_t nblocks, int64_t row_blocks,
+static bool has_signs(const Signs &sg) { return (sg.w[0] | sg.w[1] | sg.w[2] | sg.w[3]) != 0u; }
+
+int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int64_t row_blocks,
                   int64_t cache_row_blocks, int64_t t0_blocks, void *codes, void *norms,
                   void *stream)
 {
@@ -1501,39 +1546,43 @@ int launch_encode(int bits, const void *x, int64_t nblocks, int64_t row_blocks,
     hipStream_t s = (hipStream_t)stream;
     static const int per_cu = groups_per_cu("TQ_ENCODE_GROUPS_PER_CU", 2);
     dim3 grid(grid_for(nblocks, kEncTileBlocks, per_cu)), block(256);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, s, (const uint8_t *)x, (uint32_t)nblocks,
+                           (uint32_t)row_blocks, cache_row_blocks, t0_blocks, (uint8_t *)codes,
+                           (uint16_t *)norms, *cb, sg);
+    };
+    const bool rot = has_signs(sg);
     if (bits == 3)
-        hipLaunchKernelGGL(encode_kernel<3>, grid, block, 0, s, (const uint8_t *)x,
-                           (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
-                           (uint8_t *)codes, (uint16_t *)norms, *cb);
+        rot ? launch(encode_kernel<3, true>) : launch(encode_kernel<3, false>);
     else
-        hipLaunchKernelGGL(encode_kernel<2>, grid, block, 0, s, (const uint8_t *)x,
-                           (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
-                           (uint8_t *)codes, (uint16_t *)norms, *cb);
+        rot ? launch(encode_kernel<2, true>) : launch(encode_kernel<2, false>);
     return (int)hipGetLastError();
 }
 
-int launch_decode(int bits, const void *codes, const void *norms, int64_t nblocks,
-                  int64_t row_blocks, int64_t cache_row_blocks, int64_t t0_blocks, void *x,
-                  void *stream)
+int launch_decode(int bits, const Signs &sg, const void *codes, const void *norms,
+                  int64_t nblocks, int64_t row_blocks, int64_t cache_row_blocks,
+                  int64_t t0_blocks, void *x, void *stream)
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
     static const int per_cu = groups_per_cu("TQ_DECODE_GROUPS_PER_CU", 2);
     dim3 grid(grid_for(nblocks, kBlocksPerWave, per_cu)), block(256);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, s, (const uint8_t *)codes, (const uint16_t *)norms,
+                           (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
+                           (uint8_t *)x, *cb, sg);
+    };
+    const bool rot = has_signs(sg);
     if (bits == 3)
-        hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, s, (const uint8_t *)codes,
-                           (const uint16_t *)norms, (uint32_t)nblocks, (uint32_t)row_blocks,
-                           cache_row_blocks, t0_blocks, (uint8_t *)x, *cb);
+        rot ? launch(decode_kernel<3, true>) : launch(decode_kernel<3, false>);
     else
-        hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, s, (const uint8_t *)codes,
-                           (const uint16_t *)norms, (uint32_t)nblocks, (uint32_t)row_blocks,
-                           cache_row_blocks, t0_blocks, (uint8_t *)x, *cb);
+        rot ? launch(decode_kernel<2, true>) : launch(decode_kernel<2, false>);
     return (int)hipGetLastError();
 }
 
-int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int64_t Hkv,
-              int64_t Tc, int64_t m, int64_t T, const void *q, int64_t Hq, float scale,
-              float *scores, void *stream)
+int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norms, int64_t B,
+              int64_t Hkv, int64_t Tc, int64_t m, int64_t T, const void *q, int64_t Hq,
+              float scale, float *scores, void *stream)
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
@@ -1567,7 +1616,7 @@ int launch_qk(int bits, const void *k_codes, const void *k_norms, int64_t B, int
         hipLaunchKernelGGL(kern, grid, block, smem, s, (const uint8_t *)k_codes,
                            (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,
                            Tc, (uint32_t)T, (uint32_t)m, (uint32_t)G, (uint32_t)Hq,
-                           (uint32_t)passes, (uint32_t)tpg, scale, *cb);
+                           (uint32_t)passes, (uint32_t)tpg, scale, *cb, sg);
         return (int)hipGetLastError();
     };
     if (bits == 3)
@@ -1597,9 +1646,10 @@ int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_
     return B * Hq * chunks * kAttnRec * (int64_t)sizeof(float);
 }
 
-int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *v_codes,
-                const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t T,
-                const void *q, int64_t Hq, float scale, float *out, void *work, void *stream)
+int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_norms,
+                const void *v_codes, const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc,
+                int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
+                void *stream)
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
@@ -1614,19 +1664,19 @@ int launch_attn(int bits, const void *k_codes, const void *k_norms, const void *
                            (const uint8_t *)v_codes, (const uint16_t *)v_norms,
                            (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
                            (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                           scale, *cb);
+                           scale, *cb, sg);
     else
         hipLaunchKernelGGL((G > 4 ? attn_partial_kernel<2, 2> : attn_partial_kernel<2, 1>), grid,
                            block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
                            (const uint8_t *)v_codes, (const uint16_t *)v_norms,
                            (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
                            (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                           scale, *cb);
+                           scale, *cb, sg);
     int e = (int)hipGetLastError();
     if (e)
         return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
-                       (const float *)work, out, nparts);
+                       (const float *)work, out, nparts, sg);
     return (int)hipGetLastError();
 }
 

@@ -185,3 +185,45 @@ def test_binding_refuses_cpu_tensors():
     norms = torch.zeros((1, 1, 4, 1), dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU tensor"):
         tq.tq_encode(3, x, codes, norms)
+
+
+def test_rot_entry_points_validate_like_the_plain_ones(L):
+    """The _rot calls take the plain call's arguments after the sign words and reject
+    the same way before any HIP call; NULL signs are allowed (the plain rotation)."""
+    W = (ctypes.c_uint32 * 4)(0xFFFFFFFF, 0, 1, 0x80000000)
+    for signs in (W, None):
+        e = L.tq_encode_rot
+        assert e(4, signs, _p(X), 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_TYPE
+        assert e(3, signs, _p(X), 1, 1, 1, 100, _p(C), _p(N), 1, 0, None) == E_SHAPE
+        assert e(3, signs, _p(X), 1, 1, 2, 128, _p(C), _p(N), 4, 3, None) == E_RANGE
+        assert e(3, signs, None, 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_NULL
+        assert e(3, signs, _p(X + 8), 1, 1, 1, 128, _p(C), _p(N), 1, 0, None) == E_ALIGN
+        assert e(3, signs, _p(X), 1, 1, 1, 128, _p(X + 128), _p(N), 1, 0, None) == E_ALIAS
+        assert e(3, signs, None, 0, 8, 16, 128, None, None, 16, 0, None) == OK
+        d = L.tq_decode_rot
+        assert d(1, signs, _p(C), _p(N), 1, 1, 1, 128, 0, 1, _p(X), None) == E_TYPE
+        assert d(3, signs, _p(C), _p(N), 1, 1, 4, 128, 2, 3, _p(X), None) == E_RANGE
+        assert d(3, signs, _p(C), _p(N), 1, 1, 1, 128, 0, 1, _p(C), None) == E_ALIAS
+        q = L.tq_qk_scores_rot
+        S4 = ctypes.cast(ctypes.c_void_p(S), ctypes.POINTER(ctypes.c_float))
+        assert q(3, signs, _p(C), _p(N), 1, 2, 8, 128, 8, _p(Q), 3, ctypes.c_float(1.0), S4, None) == E_SHAPE
+        assert q(3, signs, _p(C), _p(N), 1, 2, 8, 128, 9, _p(Q), 4, ctypes.c_float(1.0), S4, None) == E_RANGE
+        a = L.tq_attn_decode_rot
+        assert a(3, signs, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 8, 256, 8,
+                 _p(Q), 4, ctypes.c_float(1.0), S4, _p(0x60000000), 1 << 20, None) == E_SHAPE
+        assert a(3, signs, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 8, 128, 8,
+                 _p(Q), 4, ctypes.c_float(1.0), S4, _p(0x60000000), 0, None) == E_WORKSPACE
+
+
+def test_sign_words_bit_layout():
+    """Position p of a block <-> bit p % 32 of word p / 32; -1 (or True) sets the bit."""
+    d = np.ones(128)
+    d[[0, 31, 32, 100, 127]] = -1
+    w = list(tq.sign_words(d))
+    assert w == [0x80000001, 0x00000001, 0x00000000, 0x80000010]
+    assert list(tq.sign_words([v < 0 for v in d])) == w
+    assert list(tq.sign_words(np.ones(128))) == [0, 0, 0, 0]
+    with pytest.raises(ValueError):
+        tq.sign_words(np.ones(127))
+    with pytest.raises(ValueError):
+        tq.sign_words(np.full(128, 0.5))
