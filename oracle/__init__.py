@@ -69,6 +69,10 @@ def _load():
     lib.tqo_attn_decode.restype = i32
     lib.tqo_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, dbl,
                                     vp, vp, i32]
+    lib.tqo_pack_records.restype = i32
+    lib.tqo_pack_records.argtypes = [i32, vp, vp, i64, vp]
+    lib.tqo_unpack_records.restype = i32
+    lib.tqo_unpack_records.argtypes = [i32, vp, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -261,3 +265,29 @@ def attn_decode(bits: int, k_codes, k_norms, v_codes, v_norms, q, scale: float,
     if rc:
         raise ValueError("tqo_attn_decode failed")
     return out
+
+
+def pack_records(bits: int, codes, norms) -> np.ndarray:
+    """codes u8 [..., 16*bits] + norms fp16 [...] → records u8 [nb, 2 + 16*bits]."""
+    _check_bits(bits)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, code_bytes(bits))
+    norms = _c16(norms).reshape(-1)
+    nb = codes.shape[0]
+    if norms.shape[0] != nb:
+        raise ValueError("codes / norms block counts differ")
+    rec = np.zeros((nb, 2 + code_bytes(bits)), np.uint8)
+    if _load().tqo_pack_records(bits, _ptr(codes), _ptr(norms), nb, _ptr(rec)):
+        raise ValueError("tqo_pack_records failed")
+    return rec
+
+
+def unpack_records(bits: int, records):
+    """records u8 [nb, 2 + 16*bits] → (codes u8 [nb, 16*bits], norms fp16 [nb])."""
+    _check_bits(bits)
+    rec = np.ascontiguousarray(records, dtype=np.uint8).reshape(-1, 2 + code_bytes(bits))
+    nb = rec.shape[0]
+    codes = np.zeros((nb, code_bytes(bits)), np.uint8)
+    norms = np.zeros(nb, np.float16)
+    if _load().tqo_unpack_records(bits, _ptr(rec), nb, _ptr(codes), _ptr(norms)):
+        raise ValueError("tqo_unpack_records failed")
+    return codes, norms

@@ -678,3 +678,42 @@ int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
     parallel_for(B * Hkv, nthreads, attn_range, &c);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Interleaved block records.                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Section "どこまで小さくなるのか": each block packs its 128 values and one FP16
+ * norm (50 / 34 bytes).  Record layout (this oracle's reading; the page fixes
+ * only the content and the size): the norm's two bytes, little-endian, then
+ * the block's 16*bits code bytes; records in block order.  Byte copies only. */
+int tqo_pack_records(int bits, const uint8_t *codes, const uint16_t *norms, int64_t nblocks,
+                     uint8_t *records)
+{
+    if ((bits != 2 && bits != 3) || nblocks < 0)
+        return -1;
+    int cb = 16 * bits, rb = cb + 2;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        uint8_t *r = records + b * rb;
+        r[0] = (uint8_t)(norms[b] & 0xFF);
+        r[1] = (uint8_t)(norms[b] >> 8);
+        for (int i = 0; i < cb; ++i)
+            r[2 + i] = codes[b * cb + i];
+    }
+    return 0;
+}
+
+int tqo_unpack_records(int bits, const uint8_t *records, int64_t nblocks, uint8_t *codes,
+                       uint16_t *norms)
+{
+    if ((bits != 2 && bits != 3) || nblocks < 0)
+        return -1;
+    int cb = 16 * bits, rb = cb + 2;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const uint8_t *r = records + b * rb;
+        norms[b] = (uint16_t)(r[0] | (r[1] << 8));
+        for (int i = 0; i < cb; ++i)
+            codes[b * cb + i] = r[2 + i];
+    }
+    return 0;
+}

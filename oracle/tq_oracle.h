@@ -66,6 +66,13 @@ int tqo_attn_decode(int bits, const uint8_t *k_codes, const uint16_t *k_norms,
                     int64_t Tc, int64_t D, int64_t T, const uint16_t *q, int64_t Hq, double scale,
                     double *out, const double *d, int nthreads);
 
+/* Interleaved records of 2 + 16*bits bytes per block (the fp16 norm, little-
+ * endian, then the code bytes) from / to the two planes. */
+int tqo_pack_records(int bits, const uint8_t *codes, const uint16_t *norms, int64_t nblocks,
+                     uint8_t *records);
+int tqo_unpack_records(int bits, const uint8_t *records, int64_t nblocks, uint8_t *codes,
+                       uint16_t *norms);
+
 #ifdef __cplusplus
 }
 #endif

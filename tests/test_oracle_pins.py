@@ -603,3 +603,32 @@ def test_rotation_qk_and_attention_against_dense(bits):
     ref = np.einsum("bgrt,bgtd->bgrd", scipy.special.softmax(s, axis=-1), vh).reshape(B, Hkv * G, D)
     out = oracle.attn_decode(bits, kc, kn, vc, vn, q, scale, T=T, signs=d)
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- interleaved records
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_records_match_a_block_struct(bits, golden_dir):
+    """Records are the block struct {fp16 d; uint8 qs[16*bits]} in block order: checked
+    against numpy's packed structured dtype of that struct, whose item size is the
+    article's bytes per block (50 / 34, "どこまで小さくなるのか")."""
+    cb = 16 * bits
+    rec_t = np.dtype([("d", "<f2"), ("qs", "u1", (cb,))])
+    printed = {r[0]: float(r[3]) for r in _golden(golden_dir, "block_sizes.txt") if r[0].startswith("turbo")}
+    assert rec_t.itemsize == 2 + cb
+    assert round(rec_t.itemsize / 128, 2) == printed[f"turbo{bits}"]   # 0.39 / 0.27 B per value
+    rng = np.random.default_rng(30 + bits)
+    nb = 777
+    codes = rng.integers(0, 256, (nb, cb), dtype=np.uint8)
+    norms = rng.uniform(0, 300, nb).astype(np.float16)
+    rec = oracle.pack_records(bits, codes, norms)
+    view = rec.reshape(-1).view(rec_t)
+    assert np.array_equal(view["d"].view(np.uint16), norms.view(np.uint16))
+    assert np.array_equal(view["qs"], codes)
+    c2, n2 = oracle.unpack_records(bits, rec)
+    assert np.array_equal(c2, codes) and np.array_equal(n2.view(np.uint16), norms.view(np.uint16))
+    # built independently: records from the struct, unpacked by the oracle
+    s = np.zeros(nb, rec_t)
+    s["d"], s["qs"] = norms, codes
+    c3, n3 = oracle.unpack_records(bits, s.view(np.uint8))
+    assert np.array_equal(c3, codes) and np.array_equal(n3.view(np.uint16), norms.view(np.uint16))
