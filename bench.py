@@ -27,7 +27,9 @@ size (16 sequences, each with turbo3 K and V caches [8 kv heads, 32768 rows, 128
 prefilled by encode: the 1-token append of K and V at row 32767, q.K of 32 query
 heads over all rows, and the fused decode attention of the 32 heads over the
 compressed K and V); "rotation" times turbo3 encode and decode of the layer with the
-randomised rotation H D (seeded signs); "bandwidth_configs" times encode and decode of
+randomised rotation H D (seeded signs); "records" times the repack of that turbo3
+cache into interleaved 50-byte block records and back; "bandwidth_configs" times
+encode and decode of
 a whole 14B-shaped turbo3 cache and a head_dim-256 turbo2 cache.
 """
 from __future__ import annotations
@@ -202,6 +204,26 @@ def main():
         rotation[name] = {"us": round(us, 2), "bytes": nbytes,
                           "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                           "vs_plain": round(us / plain, 3)}
+
+    # interleaved 50-byte records of the same turbo3 cache (not part of the step): both
+    # directions read and write 50 bytes per block
+    rec = torch.empty(nblk * 50, dtype=torch.uint8, device=dev)
+    records = {}
+    for name, fn in (("pack_records_turbo3", lambda: tq.tq_pack_records(3, *b3["c"], rec)),
+                     ("unpack_records_turbo3", lambda: tq.tq_unpack_records(3, rec, *b3["c"]))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = 2 * nblk * 50
+        records[name] = {"us": round(us, 2), "bytes": nbytes,
+                         "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del rec
     for _ in range(2):
         step()
     torch.cuda.synchronize()
@@ -257,6 +279,7 @@ def main():
         "cpu_baseline": cpu,
         "ops": per_op,
         "rotation": rotation,
+        "records": records,
         "decode_step": dstep,
         "bandwidth_configs": bw_cfgs,
     }

@@ -143,6 +143,22 @@ int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const voi
                    const void *q, int64_t Hq, float scale, float *out, void *workspace,
                    int64_t workspace_bytes, void *stream);
 
+/* Interleaved block records (each block packs its 128 values and one FP16 norm,
+ * section "どこまで小さくなるのか": 50 B turbo3, 34 B turbo2), the llama.cpp-style
+ * block struct { fp16 norm (little-endian); uint8 codes[16*type]; }, records in block
+ * order, for interchange with code that expects one record per block:
+ *   codes    device codes plane of nblocks blocks (16*type bytes each), 16-byte aligned
+ *   norms    device norms plane of nblocks fp16 values, 2-byte aligned
+ *   records  device nblocks * (2 + 16*type) bytes, 16-byte aligned
+ * Block b of the planes <-> record b.  A sub-range of a cache is converted by passing
+ * pointers offset to its first block (records then stay 16-byte aligned for block
+ * offsets that are multiples of 8).  Requires 0 <= nblocks < 2^31.  Byte moves only:
+ * a pack followed by an unpack restores both planes exactly. */
+int tq_pack_records(int type, const void *codes, const void *norms, int64_t nblocks,
+                    void *records, void *stream);
+int tq_unpack_records(int type, const void *records, int64_t nblocks, void *codes, void *norms,
+                      void *stream);
+
 /* Randomised rotation.  TurboQuant rotates each vector by a random orthogonal matrix
  * before quantising (section "TurboQuant の何が違うのか"); the calls above use the
  * fixed Hadamard H.  The _rot variants below use H D instead, D a diagonal of signs:

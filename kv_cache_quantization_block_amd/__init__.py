@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.restype = i32
     L.tq_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp,
                                  vp, i64, vp]
+    L.tq_pack_records.restype = i32
+    L.tq_pack_records.argtypes = [i32, vp, vp, i64, vp, vp]
+    L.tq_unpack_records.restype = i32
+    L.tq_unpack_records.argtypes = [i32, vp, i64, vp, vp, vp]
     for name, plain in (("tq_encode_rot", L.tq_encode), ("tq_decode_rot", L.tq_decode),
                         ("tq_qk_scores_rot", L.tq_qk_scores), ("tq_attn_decode_rot", L.tq_attn_decode)):
         f = getattr(L, name)
@@ -274,3 +278,32 @@ def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_co
           else lib().tq_attn_decode_rot(type, sign_words(signs), *args))
     if rc:
         raise TQError(rc, "tq_attn_decode")
+
+
+def _record_args(type: int, codes: torch.Tensor, norms: torch.Tensor, records: torch.Tensor):
+    nb = norms.numel()
+    if codes.numel() != nb * 16 * type or records.numel() != nb * (2 + 16 * type):
+        raise ValueError("codes / norms / records sizes do not describe the same blocks")
+    return nb
+
+
+def tq_pack_records(type: int, codes: torch.Tensor, norms: torch.Tensor, records: torch.Tensor,
+                    stream=None) -> None:
+    """Both planes (any shape, contiguous) -> interleaved records, a uint8 tensor of
+    norms.numel() * (2 + 16 * type) bytes (asynchronous)."""
+    nb = _record_args(type, codes, norms, records)
+    rc = lib().tq_pack_records(type, _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
+                               nb, _dev(records, "records", torch.uint8), _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_pack_records")
+
+
+def tq_unpack_records(type: int, records: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
+                      stream=None) -> None:
+    """Interleaved records -> both planes (asynchronous)."""
+    nb = _record_args(type, codes, norms, records)
+    rc = lib().tq_unpack_records(type, _dev(records, "records", torch.uint8), nb,
+                                 _dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float16),
+                                 _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_unpack_records")

@@ -224,6 +224,48 @@ int tq_qk_scores(int type, const void *k_codes, const void *k_norms, int64_t B, 
                             scores, stream);
 }
 
+int tq_pack_records(int type, const void *codes, const void *norms, int64_t nblocks,
+                    void *records, void *stream)
+{
+    if (!valid_type(type))
+        return TQ_ERR_TYPE;
+    if (nblocks < 0 || nblocks > INT32_MAX)
+        return TQ_ERR_SHAPE;
+    if (nblocks == 0)
+        return TQ_OK;
+    if (!codes || !norms || !records)
+        return TQ_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(norms, 2) || !aligned(records, 16))
+        return TQ_ERR_ALIGN;
+    const int64_t cb = nblocks * 16 * type, nbytes = nblocks * 2, rb = nblocks * (2 + 16 * type);
+    if (overlap(records, rb, codes, cb) || overlap(records, rb, norms, nbytes))
+        return TQ_ERR_ALIAS;
+    return tq::launch_pack_records(type, codes, norms, nblocks, records, stream) ? TQ_ERR_DEVICE
+                                                                                : TQ_OK;
+}
+
+int tq_unpack_records(int type, const void *records, int64_t nblocks, void *codes, void *norms,
+                      void *stream)
+{
+    if (!valid_type(type))
+        return TQ_ERR_TYPE;
+    if (nblocks < 0 || nblocks > INT32_MAX)
+        return TQ_ERR_SHAPE;
+    if (nblocks == 0)
+        return TQ_OK;
+    if (!codes || !norms || !records)
+        return TQ_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(norms, 2) || !aligned(records, 16))
+        return TQ_ERR_ALIGN;
+    const int64_t cb = nblocks * 16 * type, nbytes = nblocks * 2, rb = nblocks * (2 + 16 * type);
+    if (overlap(records, rb, codes, cb) || overlap(records, rb, norms, nbytes) ||
+        overlap(codes, cb, norms, nbytes))
+        return TQ_ERR_ALIAS;
+    return tq::launch_unpack_records(type, records, nblocks, codes, norms, stream)
+               ? TQ_ERR_DEVICE
+               : TQ_OK;
+}
+
 }  // extern "C"
 
 // Shapes of the decode attention call (D = 128); fills the cache blocks of one cache.

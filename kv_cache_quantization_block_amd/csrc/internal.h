@@ -59,4 +59,11 @@ int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_no
                 int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
                 void *stream);
 
+// Interleaved records (2 + 16 bits bytes per block) from / to the two planes,
+// nblocks < 2^31.
+int launch_pack_records(int bits, const void *codes, const void *norms, int64_t nblocks,
+                        void *records, void *stream);
+int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *codes,
+                          void *norms, void *stream);
+
 }  // namespace tq

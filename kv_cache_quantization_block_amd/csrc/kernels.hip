@@ -1496,6 +1496,108 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
     out[(size_t)bh * kBlock + 64 + lane] = __builtin_bit_cast(float, uc);
 }
 
+// ---------------------------------------------------------------- interleaved records
+//
+// A block as one record of 2 + 16 BITS bytes: its fp16 norm (little-endian), then its
+// code bytes, records in block order (each block packs 128 values and one FP16 norm,
+// 50 / 34 bytes: the article's size section).  Both directions are byte moves bound
+// by HBM: a wave takes a tile of 64 blocks, reads it with 16-byte loads into LDS, and
+// writes the other layout with 16-byte stores, gathering halfwords from LDS (records
+// are 2-byte granular).  A tile of 64 records starts 16-byte aligned (64 x 50 and 64 x
+// 34 are multiples of 16); the last tile's ragged end goes out halfword by halfword.
+
+constexpr int kRecTile = 64;   // blocks per wave tile
+
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_records_kernel(const uint8_t *__restrict__ codes,
+                                                           const uint16_t *__restrict__ norms,
+                                                           uint32_t nblocks,
+                                                           uint8_t *__restrict__ rec)
+{
+    constexpr int CB = 16 * BITS, RH = CB / 2 + 1;   // code bytes, halfwords per record
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWavesPerGroup][kRecTile * (CB + 2)];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t b0 = (blockIdx.x * kWavesPerGroup + wave) * kRecTile;
+    if (b0 >= nblocks)
+        return;
+    const uint32_t nb = min(nblocks - b0, (uint32_t)kRecTile);
+    uint8_t *lc = lds_all[wave];                              // codes [64][CB]
+    uint16_t *ln = (uint16_t *)(lc + kRecTile * CB);          // norms [64]
+    const u4_t *src = (const u4_t *)(codes + (size_t)b0 * CB);
+    const uint32_t nch = nb * (CB / 16);
+    for (uint32_t c = lane; c < nch; c += 64u)
+        *(u4_t *)(lc + c * 16u) = ld_stream(src + c);
+    if (lane < nb)
+        ln[lane] = ld_stream(norms + b0 + lane);
+    wave_lds_sync();
+
+    const uint16_t *lc16 = (const uint16_t *)lc;
+    const uint32_t nh = nb * RH;                              // halfwords of the tile's records
+    uint8_t *dst = rec + (size_t)b0 * (CB + 2);
+    for (uint32_t h = 8u * lane; h < nh; h += 512u) {
+        uint32_t r = h / RH, k = h - r * RH;
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = h + i < nh ? (k == 0 ? ln[r] : lc16[r * (CB / 2) + k - 1]) : 0u;
+            if (++k == (uint32_t)RH) {
+                k = 0;
+                ++r;
+            }
+        }
+        if (h + 8u <= nh) {
+            *(u4_t *)(dst + 2u * h) = u4_t{v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16,
+                                           v[6] | v[7] << 16};
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (h + i < nh)
+                    ((uint16_t *)dst)[h + i] = (uint16_t)v[i];
+        }
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_records_kernel(const uint8_t *__restrict__ rec,
+                                                             uint32_t nblocks,
+                                                             uint8_t *__restrict__ codes,
+                                                             uint16_t *__restrict__ norms)
+{
+    constexpr int CB = 16 * BITS, RH = CB / 2 + 1;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWavesPerGroup][kRecTile * (CB + 2)];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t b0 = (blockIdx.x * kWavesPerGroup + wave) * kRecTile;
+    if (b0 >= nblocks)
+        return;
+    const uint32_t nb = min(nblocks - b0, (uint32_t)kRecTile);
+    uint8_t *lr = lds_all[wave];
+    const uint8_t *srcb = rec + (size_t)b0 * (CB + 2);
+    const uint32_t nh = nb * RH, nfull = nh / 8u;             // whole 16-byte chunks, then halfwords
+    for (uint32_t c = lane; c < nfull; c += 64u)
+        *(u4_t *)(lr + c * 16u) = ld_stream((const u4_t *)srcb + c);
+    if (8u * nfull + lane < nh)
+        ((uint16_t *)lr)[8u * nfull + lane] = ld_stream((const uint16_t *)srcb + 8u * nfull + lane);
+    wave_lds_sync();
+
+    const uint16_t *lr16 = (const uint16_t *)lr;
+    constexpr uint32_t CPB = CB / 16;                         // 16-byte code chunks per block
+    uint8_t *dstc = codes + (size_t)b0 * CB;
+    for (uint32_t c = lane; c < nb * CPB; c += 64u) {
+        const uint32_t r = c / CPB, j = c - r * CPB;
+        const uint16_t *p = lr16 + r * RH + 1u + 8u * j;
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = p[i];
+        *(u4_t *)(dstc + 16u * c) = u4_t{v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16,
+                                         v[6] | v[7] << 16};
+    }
+    if (lane < nb)
+        norms[b0 + lane] = lr16[lane * RH];
+}
+
 // Compute units of the current device (cached per device).
 int cu_count()
 {
@@ -1628,6 +1730,36 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
 // Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
 // device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
 // of kAttnDepth units per wave, at most 65535 chunks.
+int launch_pack_records(int bits, const void *codes, const void *norms, int64_t nblocks,
+                        void *records, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t tiles = (nblocks + kRecTile - 1) / kRecTile;
+    dim3 grid((uint32_t)((tiles + kWavesPerGroup - 1) / kWavesPerGroup)), block(256);
+    if (bits == 3)
+        hipLaunchKernelGGL(pack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)codes,
+                           (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
+    else
+        hipLaunchKernelGGL(pack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)codes,
+                           (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
+    return (int)hipGetLastError();
+}
+
+int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *codes,
+                          void *norms, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t tiles = (nblocks + kRecTile - 1) / kRecTile;
+    dim3 grid((uint32_t)((tiles + kWavesPerGroup - 1) / kWavesPerGroup)), block(256);
+    if (bits == 3)
+        hipLaunchKernelGGL(unpack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)records,
+                           (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
+    else
+        hipLaunchKernelGGL(unpack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)records,
+                           (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
+    return (int)hipGetLastError();
+}
+
 int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;

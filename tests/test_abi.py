@@ -227,3 +227,24 @@ def test_sign_words_bit_layout():
         tq.sign_words(np.ones(127))
     with pytest.raises(ValueError):
         tq.sign_words(np.full(128, 0.5))
+
+
+def test_record_validation(L):
+    p, u = L.tq_pack_records, L.tq_unpack_records
+    R = 0x70000000
+    assert p(4, _p(C), _p(N), 8, _p(R), None) == E_TYPE
+    assert p(3, _p(C), _p(N), -1, _p(R), None) == E_SHAPE
+    assert p(3, _p(C), _p(N), 1 << 31, _p(R), None) == E_SHAPE
+    assert p(3, None, _p(N), 8, _p(R), None) == E_NULL
+    assert p(3, _p(C + 8), _p(N), 8, _p(R), None) == E_ALIGN
+    assert p(3, _p(C), _p(N + 1), 8, _p(R), None) == E_ALIGN
+    assert p(3, _p(C), _p(N), 8, _p(R + 2), None) == E_ALIGN
+    assert p(3, _p(C), _p(N), 8, _p(C + 16), None) == E_ALIAS
+    assert p(2, None, None, 0, None, None) == OK
+    assert u(1, _p(R), 8, _p(C), _p(N), None) == E_TYPE
+    assert u(3, _p(R), -5, _p(C), _p(N), None) == E_SHAPE
+    assert u(3, _p(R), 8, _p(C), None, None) == E_NULL
+    assert u(3, _p(R + 4), 8, _p(C), _p(N), None) == E_ALIGN
+    assert u(3, _p(R), 8, _p(C), _p(C + 384 - 2), None) == E_ALIAS      # norms inside the codes
+    assert u(3, _p(R), 8, _p(R + 16), _p(N), None) == E_ALIAS
+    assert u(3, None, 0, None, None, None) == OK
