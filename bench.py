@@ -286,16 +286,17 @@ def main():
     print(json.dumps(out))
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_turbo3_one_layer_kv_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "one_layer_kv_kernels_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_quantization_block_amd", "csrc", "kernels.hip")
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or None when no
-    summary covers this kernel or the kernel source changed since it was taken."""
+    """HBM bytes per launch of op `kernel` (encode_turbo3, decode_turbo3, ...) from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy of
+    known size), or None when the summary does not cover this op or the kernel source
+    changed since it was taken."""
     import hashlib
-    if kernel != "encode_turbo3" or not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = {}
     for line in open(TRAFFIC_FILE):
@@ -304,11 +305,11 @@ def measured_traffic(kernel: str):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
     sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != sha:
+    if rec.get("kernel_source_sha256_16") != sha or f"{kernel}.fetch_size_kib" not in rec:
         return None
     copy_kib = int(rec["copy_bytes"]) / 1024
-    fetch = float(rec["fetch_size_kib"]) * copy_kib / float(rec["copy_fetch_size_kib"])
-    write = float(rec["write_size_kib"]) * copy_kib / float(rec["copy_write_size_kib"])
+    fetch = float(rec[f"{kernel}.fetch_size_kib"]) * copy_kib / float(rec["copy_fetch_size_kib"])
+    write = float(rec[f"{kernel}.write_size_kib"]) * copy_kib / float(rec["copy_write_size_kib"])
     return int(round((fetch + write) * 1024))
 
 

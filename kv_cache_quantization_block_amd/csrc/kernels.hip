@@ -45,6 +45,8 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));   // a matrix-core fp16 operand
+typedef float f4_t __attribute__((ext_vector_type(4)));      // a 16 x 16 product's four rows
 
 constexpr int kTileBytes = kBlocksPerWave * kBlock * 2;   // 16 KB of fp16 per wave
 
@@ -87,21 +89,6 @@ __device__ __forceinline__ T lds_load(uint32_t addr)
 // each reading its own copy, never collide whatever entries they pick.
 constexpr int kLdsCopies8 = 32;
 
-// d = a.x * b.x + a.y * b.y + c in the three-operand VOP3P form (the compiler's
-// accumulate-in-place form would need a register copy per result here).
-// fp16 x (+-1) products are exact, the sum is a float.
-__device__ __forceinline__ float dot2(h2_t a, h2_t b, float c)
-{
-    float d;
-    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
-}
-__device__ __forceinline__ float dot2(h2_t a, h2_t b)
-{
-    float d;
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
-    return d;
-}
 
 // The value of another lane of the same quad (DPP quad_perm pattern CTRL).
 template <int CTRL>
@@ -209,36 +196,9 @@ __device__ __forceinline__ int64_t cache_block(uint32_t b, uint32_t row_blocks,
 // (W = waves in the grid), prefetching tile i + W while it computes tile i, so
 // HBM traffic and VALU work of different tiles overlap inside every wave.
 
-// ---------------------------------------------------------------- encode
-//
-// Two lanes per block: lane l holds half h = l / 32 (values 64 h .. 64 h + 63) of
-// block l % 32 of a 32-block (8 KB) wave tile.  The butterfly stages of spans 1..32
-// run inside each lane; the span-64 stage pairs the two halves: one
-// v_permlane32_swap per two registers brings value i of the partner next to value
-// i of this lane, after which the butterfly is again in-lane.  A lane then owns the
-// outputs of positions [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h), i.e. two
-// 32-code groups that are whole 12-byte (turbo3) / 8-byte (turbo2) runs of the
-// packed block, so no code ever crosses lanes.  64 floats per lane keep a wave
-// under 168 VGPRs: three waves per SIMD, each with the next tile in flight.
-
+// Encode tiles: 32 blocks per wave (two 16-block column tiles of the matrix-core
+// rotation below); the staged codes of a tile leave as 16-byte stores.
 constexpr int kEncTileBlocks = 32;
-constexpr int kEncTileBytes = kEncTileBlocks * kBlock * 2;   // 8 KB of fp16
-
-// R[k] = chunk (lane % 16) of block 4 k + lane / 16 of the tile; zeros past nb.
-__device__ __forceinline__ void load_enc_tile(u4_t (&R)[8], const uint8_t *__restrict__ x,
-                                              uint32_t b0, uint32_t nb, uint32_t lane)
-{
-    const uint8_t *src = x + (size_t)b0 * (kBlock * 2) + lane * 16;
-    if (nb == kEncTileBlocks) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            R[k] = ld_stream((const u4_t *)(src + k * 1024));
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            R[k] = 4 * k + (lane >> 4) < nb ? ld_stream((const u4_t *)(src + k * 1024)) : u4_t{0, 0, 0, 0};
-    }
-}
 
 // (upper 32 lanes of a) <-> (lower 32 lanes of b), returned as the new (a, b).
 __device__ __forceinline__ void swap32(float &a, float &b)
@@ -317,194 +277,174 @@ __device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t la
     }
 }
 
-// Per iteration (tile i): park tile i in LDS, write out tile i-1 (finished in the
-// previous iteration), issue the loads of tile i+1, then compute tile i.  The
-// stores and the next loads are both issued before the compute, so neither the
-// load latency nor the store completions hold the wave at its next wait.
-// ROT: rotate by H D (Signs sg) instead of H: a lane's 16-byte loads always hold the
-// same eight positions of a block (chunk lane % 16), so D is one XOR per packed pair
-// before the tile is parked in LDS.
+// ---------------------------------------------------------------- encode
+//
+// The rotation u = H x is a dense contraction with a +-1 matrix, and Sylvester's H
+// factors over the index split p = 32 g + q as H_128 = H_4 (x) H_32:
+//   v_g'[q]     = sum_q' H_32[q][q'] x[32 g' + q']     (matrix cores, v_mfma_f32_16x16x32_f16:
+//                                                        fp16 inputs, +-1 weights, exact
+//                                                        products summed in fp32)
+//   u[32 g + q] = sum_g' H_4[g][g'] v_g'[q]             (two butterfly stages per value)
+// which replaces the seven butterfly stages of the VALU encoder by two.  A wave takes
+// 32 blocks as two 16-block column tiles.  Column n of a product is block 16 c + n;
+// the k-slots of lane group G (lane / 16) are values 32 g' + 8 G .. + 7 of that block,
+// one 16-byte load that is the B operand as loaded.  Row i of row tile r is H_32 row
+// 8 (i / 4) + 4 r + i % 4, so lane group G receives q = 8 G .. 8 G + 7 of every g':
+// after the butterflies it holds positions 32 g + 8 G .. + 7 for g = 0..3, four runs of
+// eight codes (24 / 16 bits, byte aligned), which go to the staged tile by byte writes.
+// The norm's sum of squares comes from the same loads (v_dot2 of exact fp16 squares)
+// and is summed over the four lane groups of a block in one fixed order.
 template <int BITS, bool ROT>
 __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restrict__ x,
-                                                        uint32_t nblocks, uint32_t row_blocks,
-                                                        int64_t cache_row_blocks,
-                                                        int64_t t0_blocks,
-                                                        uint8_t *__restrict__ codes,
-                                                        uint16_t *__restrict__ norms, Codebook cb,
-                                                        Signs sg)
+                                                            uint32_t nblocks, uint32_t row_blocks,
+                                                            int64_t cache_row_blocks,
+                                                            int64_t t0_blocks,
+                                                            uint8_t *__restrict__ codes,
+                                                            uint16_t *__restrict__ norms,
+                                                            Codebook cb, Signs sg)
 {
-    constexpr int GW = BITS;              // 32-bit words per 32-code group
-    constexpr int GB = 4 * BITS;          // bytes per 32-code group
     constexpr int CB = 16 * BITS;         // code bytes per block
-    constexpr int kStage = kEncTileBlocks * 48;
     constexpr float mid = (float)(1 << (BITS - 1));
-    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWavesPerGroup][kEncTileBytes + kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWavesPerGroup][kEncTileBlocks * 48];
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
-    const uint32_t blk = lane & 31u, half = lane >> 5;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n = lane & 15u, G = lane >> 4;
     const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
     const uint32_t stride = gridDim.x * kWavesPerGroup;
     uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
     if (tile >= ntiles)
         return;
-    uint8_t *lds = lds_all[wave];
-    uint8_t *stage = lds + kEncTileBytes;
+    uint8_t *stage = stage_all[wave];
 
-    u4_t R[8];
-    load_enc_tile(R, x, tile * kEncTileBlocks, min(nblocks - tile * kEncTileBlocks, 32u), lane);
-    const u4_t smask = ROT ? sign_mask_chunk(sg, lane & 15u) : u4_t{0, 0, 0, 0};
+    // A operands: row tile r, lane row n -> H_32 row q = 8 (n / 4) + 4 r + n % 4, k-slots
+    // 8 G + s: +-1 as fp16 (sign bit of (-1)^popcount(q & k))
+    h8_t A[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint32_t q = 8u * (n >> 2) + 4u * r + (n & 3u);
+        uint32_t w[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const uint32_t k0 = 8u * G + 2u * s2;
+            const uint32_t h0 = (__builtin_popcount(q & k0) & 1u) ? 0xBC00u : 0x3C00u;
+            const uint32_t h1 = (__builtin_popcount(q & (k0 + 1u)) & 1u) ? 0xBC00u : 0x3C00u;
+            w[s2] = h0 | (h1 << 16);
+        }
+        A[r] = __builtin_bit_cast(h8_t, u4_t{w[0], w[1], w[2], w[3]});
+    }
+    // randomised rotation: the chunk of load (c, g') is 4 g' + G of its block
+    u4_t smask[4];
+#pragma unroll
+    for (int gp = 0; gp < 4; ++gp)
+        smask[gp] = ROT ? sign_mask_chunk(sg, 4u * gp + G) : u4_t{0, 0, 0, 0};
+
+    // loads of column tile c of a tile: R[c][g'] = values 32 g' + 8 G .. + 7 of block
+    // b0 + 16 c + n (zeros past the tile's blocks)
+    u4_t R[2][4];
+    auto load_col = [&](uint32_t t, int c) {
+        const uint32_t b0 = t * kEncTileBlocks;
+        const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
+        const uint32_t b = 16u * c + n;
+        const u4_t *src = (const u4_t *)(x + ((size_t)b0 + b) * (kBlock * 2) + 16u * G);
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp)
+            R[c][gp] = b < nb ? ld_stream(src + 4 * gp) : u4_t{0, 0, 0, 0};
+    };
+    load_col(tile, 0);
+    load_col(tile, 1);
     uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in `stage`
     uint16_t pn16 = 0;
     for (;;) {
         const uint32_t b0 = tile * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
-
-        // 1. park the tile in LDS (XOR-swizzled); write out the previous tile; then
-        //    start loading the next one into R
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *(u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u)) = ROT ? R[k] ^ smask : R[k];
-        wave_lds_sync();
-        if (pnb)
-            store_enc_tile<BITS>(stage, lane, pb0, pnb, pn16, row_blocks, cache_row_blocks,
-                                 t0_blocks, codes, norms);
         const uint32_t next = tile + stride;
-        if (next < ntiles)
-            load_enc_tile(R, x, next * kEncTileBlocks,
-                          min(nblocks - next * kEncTileBlocks, (uint32_t)kEncTileBlocks), lane);
-
-        // 2. this lane's half block: 64 fp16 values as 32 pairs
-        h2_t v[32];
+        float nrm[2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const u4_t wv = *(const u4_t *)(lds + swz(blk, 8 * half + c));
-            v[4 * c + 0] = as_h2(wv.x);
-            v[4 * c + 1] = as_h2(wv.y);
-            v[4 * c + 2] = as_h2(wv.z);
-            v[4 * c + 3] = as_h2(wv.w);
-        }
-
-        // 3. rotation, with the norm's sum of squares (exact fp16 squares, four
-        //    partial sums) taken from the same pairs.  Spans 1 and 2 come straight
-        //    from the fp16 pairs; the results at positions with bit 1 set come out
-        //    negated (p - (x0 + x1) instead of (x0 + x1) - p), and every later stage
-        //    only combines positions that agree in bit 1, so u[r] ends as -(H x)
-        //    wherever r & 2 (exact negations).
-        float u[64];
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-            const h2_t pm = {(_Float16)1.0f, (_Float16)-1.0f};
-            const h2_t mm = {(_Float16)-1.0f, (_Float16)-1.0f};
-            const h2_t mp = {(_Float16)-1.0f, (_Float16)1.0f};
+        for (int c = 0; c < 2; ++c) {
+            // 1. products v_g' of this column tile and its sums of squares, then the
+            //    next tile's loads into the same registers
+            f4_t D[4][2];
+            float acc[2] = {0.0f, 0.0f};
 #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                acc[(2 * g) & 3] = __builtin_amdgcn_fdot2(v[2 * g], v[2 * g], acc[(2 * g) & 3], false);
-                acc[(2 * g + 1) & 3] =
-                    __builtin_amdgcn_fdot2(v[2 * g + 1], v[2 * g + 1], acc[(2 * g + 1) & 3], false);
-                const float p = dot2(v[2 * g + 1], one);   //  x2 + x3
-                const float q = dot2(v[2 * g + 1], pm);    //  x2 - x3
-                u[4 * g + 0] = dot2(v[2 * g], one, p);     //  (x0 + x1) + (x2 + x3)
-                u[4 * g + 1] = dot2(v[2 * g], pm, q);      //  (x0 - x1) + (x2 - x3)
-                u[4 * g + 2] = dot2(v[2 * g], mm, p);      // -((x0 + x1) - (x2 + x3))
-                u[4 * g + 3] = dot2(v[2 * g], mp, q);      // -((x0 - x1) - (x2 - x3))
+            for (int gp = 0; gp < 4; ++gp) {
+                const u4_t xv = ROT ? R[c][gp] ^ smask[gp] : R[c][gp];
+                const h8_t B = __builtin_bit_cast(h8_t, xv);
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+                    D[gp][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A[r], B, f4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                acc[0] = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(xv.x), acc[0], false);
+                acc[1] = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(xv.y), acc[1], false);
+                acc[0] = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(xv.z), acc[0], false);
+                acc[1] = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(xv.w), acc[1], false);
             }
-        }
-        float ssh = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        float sso = ssh;
-        swap32(ssh, sso);   // low lanes: sso = partner's sum; high lanes: ssh = partner's sum
-        const float ss = half ? (sso + ssh) : (ssh + sso);   // same order in both lanes
-        const float n = __builtin_sqrtf(ss);
+            if (next < ntiles)
+                load_col(next, c);
+            if (c == 0) {   // 2. write out the previous tile before its bytes are reused
+                if (pnb)
+                    store_enc_tile<BITS>(stage, lane, pb0, pnb, pn16, row_blocks, cache_row_blocks,
+                                         t0_blocks, codes, norms);
+                wave_lds_sync();
+            }
+
+            // 3. the block's norm: the four lane groups add their partial sums in one
+            //    order (each addition is commutative, so all four lanes agree)
+            const float ssl = acc[0] + acc[1];
+            const float a = ssl + __shfl_xor(ssl, 16, 64);
+            const float nn = __builtin_sqrtf(a + __shfl_xor(a, 32, 64));
+            nrm[c] = nn;
+
+            // 4. butterflies over g', decision, packing, staging
+            const float rn = nn > 0.0f ? __builtin_amdgcn_rcpf(nn) : 0.0f;
+            const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
+            const float hi = cb.clamp_t * nn, lo = -hi;
+            constexpr float magic = 8388608.0f + mid;   // 2^23 + 2^b/2, exact
+            uint32_t fb[4][8];                           // [g][position 8 G + i]: 2^23 + code
+            set_f32_round_down();
 #pragma unroll
-        for (int h = 4; h < 64; h <<= 1)
+            for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int i = 0; i < 64; i += 2 * h)
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = D[0][r][j], v1 = D[1][r][j], v2 = D[2][r][j], v3 = D[3][r][j];
+                    const float a0 = v0 + v1, a1 = v0 - v1, a2 = v2 + v3, a3 = v2 - v3;
+                    const float u[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
 #pragma unroll
-                for (int j = i; j < i + h; ++j) {
-                    const float a = u[j], b = u[j + h];
-                    u[j] = a + b;
-                    u[j + h] = a - b;
+                    for (int g = 0; g < 4; ++g) {
+                        const float uc = __builtin_amdgcn_fmed3f(u[g], lo, hi);
+                        float F;
+                        if constexpr (BITS == 3) {
+                            float pp = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
+                            pp = __builtin_fmaf(__builtin_fabsf(uc), pp, k1);
+                            F = __builtin_fmaf(uc, pp, magic);
+                        } else {
+                            F = __builtin_fmaf(uc, k1, magic);
+                        }
+                        fb[g][4 * r + j] = __builtin_bit_cast(uint32_t, F);
+                    }
                 }
-        // span 64 across the two halves: after the swap, the low lane holds positions
-        // (i, 64 + i) and the high lane (32 + i, 96 + i) in (u[i], u[i + 32])
+            set_f32_round_nearest();
+            uint8_t *sb = stage + (16u * c + n) * CB;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            swap32(u[i], u[i + 32]);
-            const float a = u[i], b = u[i + 32];
-            u[i] = a + b;
-            u[i + 32] = a - b;
-        }
-
-        // 4. quantise t = u / n:  F = 2^b/2 + g(clamp(t)), code = floor(F).  The
-        //    coefficients absorb 1/n and the clamp is scaled by n, so no division per
-        //    value; g is odd, so a negated u[r] negates the last product.  n == 0
-        //    (zero block) gives F = 2^b/2 for every value.  The last FMA adds 2^23 and
-        //    runs with float rounding toward -infinity, so its result is 2^23 + floor(F)
-        //    exactly and the code sits in the low mantissa bits (F stays in [0, 2^b)).
-        const float rn = n > 0.0f ? __builtin_amdgcn_rcpf(n) : 0.0f;
-        const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
-        const float hi = cb.clamp_t * n, lo = -hi;
-        constexpr float magic = 8388608.0f + mid;   // 2^23 + 2^b/2, exact
-        uint32_t fb[64];                             // bits of 2^23 + code
-        set_f32_round_down();
-#pragma unroll
-        for (int r = 0; r < 64; ++r) {
-            const float uc = __builtin_amdgcn_fmed3f(u[r], lo, hi);
-            const float ui = (r & 2) ? -uc : uc;
-            float F;
-            if constexpr (BITS == 3) {
-                // g(t) = t * (g1 + g2 |t| + g3 t^2)
-                float p = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
-                p = __builtin_fmaf(__builtin_fabsf(uc), p, k1);
-                F = __builtin_fmaf(ui, p, magic);
-            } else {
-                F = __builtin_fmaf(ui, k1, magic);
-            }
-            fb[r] = __builtin_bit_cast(uint32_t, F);
-        }
-        set_f32_round_nearest();
-        // pack: 8 codes at a time by shift-and-add on the raw bits (the 2^23 exponent
-        // bits stay at bit 24 and above), then byte-splice the 8-code chunks into the
-        // LSB-first stream of each 32-code group
-        uint32_t wa[GW], wb[GW];   // groups r in [0, 32) and [32, 64)
-#pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-            uint32_t ch[4];
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int r0 = 32 * grp + 8 * qd;
-                uint32_t c = fb[r0 + 7];
+            for (int g = 0; g < 4; ++g) {
+                uint32_t run = fb[g][7];
 #pragma unroll
                 for (int i = 6; i >= 0; --i)
-                    c = lshl_add<BITS>(c, fb[r0 + i]);
-                ch[qd] = c;
-            }
-            uint32_t *w = grp ? wb : wa;
-            if constexpr (BITS == 3) {   // 24-bit chunks
-                w[0] = __builtin_amdgcn_perm(ch[1], ch[0], 0x04020100u);
-                w[1] = __builtin_amdgcn_perm(ch[2], ch[1], 0x05040201u);
-                w[2] = __builtin_amdgcn_perm(ch[3], ch[2], 0x06050402u);
-            } else {                     // 16-bit chunks
-                w[0] = __builtin_amdgcn_perm(ch[1], ch[0], 0x05040100u);
-                w[1] = __builtin_amdgcn_perm(ch[3], ch[2], 0x05040100u);
-            }
-        }
-
-        // 5. stage the packed groups at their place in the block (low lane: code bytes
-        //    [0, GB) and [2 GB, 3 GB); high lane: [GB, 2 GB) and [3 GB, 4 GB)); they
-        //    leave at the start of the next iteration (or after the loop)
-        {
-            uint32_t *st = (uint32_t *)(stage + blk * CB + GB * half);
-#pragma unroll
-            for (int k = 0; k < GW; ++k) {
-                st[k] = wa[k];
-                st[2 * GW + k] = wb[k];
+                    run = lshl_add<BITS>(run, fb[g][i]);
+                if constexpr (BITS == 3) {   // 24 bits at byte 12 g + 3 G
+                    uint8_t *d = sb + 12 * g + 3u * G;
+                    d[0] = (uint8_t)run;
+                    d[1] = (uint8_t)(run >> 8);
+                    d[2] = (uint8_t)(run >> 16);
+                } else {                     // 16 bits at byte 8 g + 2 G
+                    *(uint16_t *)(sb + 8 * g + 2u * G) = (uint16_t)run;
+                }
             }
         }
         pb0 = b0;
         pnb = nb;
-        pn16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf(n, 65504.0f));
-        wave_lds_sync();   // staged codes visible; this tile's LDS reads are done
+        // store_enc_tile writes block (lane & 31)'s norm from this lane
+        pn16 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf((G & 1u) ? nrm[1] : nrm[0], 65504.0f));
+        wave_lds_sync();   // staged codes visible
         tile = next;
         if (tile >= ntiles)
             break;
@@ -706,8 +646,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
 // 6 code bits for turbo3, one 16-byte entry of a four-value table indexed by 8 code
 // bits for turbo2.
 
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
 
 // (group, block) units whose codes are in flight while the previous ones are
 // scored; a group is the 16 tokens one wave scores at once.
