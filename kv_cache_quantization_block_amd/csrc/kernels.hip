@@ -931,8 +931,10 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
         }
     };
     h8_t A[8];
-    if constexpr (ONE_BLOCK)
+    if constexpr (ONE_BLOCK) {
         load_a(0, A);
+        __syncthreads();   // every wave holds its operands: qa is free for the score stages
+    }
     // LDS address of this lane's table copy (entries are addressed as integers so that
     // each lookup is one bit-field extract and one shift-add)
     const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)table + (lane % NC) * EB;
@@ -941,6 +943,14 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     const float pw_u = pw_s[hu], pw_v = pw_s[hu + 2];
     float* const out_u = scores + ((size_t)b * Hq + h0 + hu) * T;
     float* const out_v = scores + ((size_t)b * Hq + h0 + hu + 2) * T;
+    // D == 128: the scores of two units (32 rows x 8 heads) gather in a 1 KB stage per
+    // wave (the query operands' LDS, free once they are in registers) and leave as one
+    // store of 16 bytes per lane, a whole 128-byte line per head (lane l: head l / 8,
+    // rows 4 (l % 8) .. + 3)
+    float *stg = (float *)qa + wave * (kQkHeads * 32);
+    const bool rows16 = (T & 3u) == 0u && ((uintptr_t)scores & 15u) == 0u;   // rows 16-byte aligned
+    const uint32_t sh = lane >> 3, sr = 4u * (lane & 7u);
+    float *const out_s = scores + ((size_t)b * Hq + h0 + sh) * T;
 
     f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (uint32_t k0 = 0; k0 < nunits; k0 += kQkDepth) {
@@ -984,15 +994,36 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                 swap32(s0, s1);
                 swap32(s2, s3);
                 const float u = (s0 + s1) * pw_u, v = (s2 + s3) * pw_v;
-                const uint32_t t = first + gi * 16u + n;
-                if (t < last) {
-                    if (hu < nh)
-                        out_u[t] = u;
-                    if (hu + 2u < nh)
-                        out_v[t] = v;
-                }
-                if constexpr (!ONE_BLOCK)
+                if constexpr (ONE_BLOCK) {
+                    stg[hu * 32 + 16 * (d & 1) + n] = u;
+                    stg[(hu + 2) * 32 + 16 * (d & 1) + n] = v;
+                    if (d & 1) {
+                        wave_lds_sync();
+                        const float4 sv = *(const float4 *)(stg + sh * 32 + sr);
+                        const uint32_t t = first + (gi - 1u) * 16u + sr;   // the pair's first row + sr
+                        if (sh < nh) {
+                            if (rows16 && t + 3u < last) {
+                                *(float4 *)(out_s + t) = sv;
+                            } else {
+                                const float e[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (t + i < last)
+                                        out_s[t + i] = e[i];
+                            }
+                        }
+                        wave_lds_sync();   // the stage is read before the next pair writes it
+                    }
+                } else {
+                    const uint32_t t = first + gi * 16u + n;
+                    if (t < last) {
+                        if (hu < nh)
+                            out_u[t] = u;
+                        if (hu + 2u < nh)
+                            out_v[t] = v;
+                    }
                     acc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
             }
         }
     }
