@@ -9,31 +9,35 @@
 // per block.  Section "現在の実装と、これから": decode to fp16 before attention,
 // and the fused read that scores queries without materialising fp16 keys.
 //
-// Mapping on CDNA4 (wave64, 4 SIMDs x 16 lanes per CU, 160 KB LDS per CU):
-//  * encode / decode: a wavefront owns a tile of consecutive blocks (encode: 32
-//    blocks, two lanes per block; decode: 64 blocks, one per lane).  The fp16
-//    values move between HBM and the wave with fully coalesced 16-byte accesses
-//    (every load / store instruction covers 1 KB contiguous) and are transposed
-//    through a wave-private, XOR-swizzled LDS tile, so each lane then holds its
-//    values and the butterfly stages run inside its registers; the encoder's
-//    one cross-lane stage (span 64) is a v_permlane32_swap.
-//  * the first two butterfly stages of the encoder are done on the fp16
-//    inputs with v_dot2_f32_f16 against (1, 1) / (1, -1): exact products,
-//    float accumulation, the fp16 -> f32 conversion folded in.
+// Mapping on CDNA4 (wave64, 4 SIMDs x 16 lanes per CU, 160 KB LDS per CU, matrix
+// cores per SIMD):
+//  * encode: a wave owns 32 consecutive blocks.  The rotation's H_32 factor runs on
+//    the matrix cores straight from the fp16 loads (+-1 weights: exact products,
+//    fp32 sums), the H_4 factor as two butterfly stages in registers; the norm's
+//    sum of squares comes from the same registers by v_dot2.
 //  * the quantiser is one clamp and three FMAs per value (turbo2: one): an odd
 //    polynomial that crosses k exactly at the k-th positive threshold maps t to
 //    2^b/2 + g(t), whose floor is the code; the last FMA adds 2^23 under
 //    round-toward-minus-infinity, which leaves the floor in the low mantissa
 //    bits, and eight codes are then packed by seven shift-adds.
-//  * decode reads stage-one (turbo3) or stage-two (turbo2) outputs straight
-//    from a small LDS table indexed by 6 / 8 packed code bits.
-//  * q.K: q . (H y) = (H q) . y since H is symmetric, so each query slice is
-//    rotated once per workgroup and every key token is scored with a table
-//    lookup and one FMA per (value, query head); the decoded key is never
-//    formed.  Four lanes share one 128-value key block; a wave scores 16 key
-//    rows of one kv head for up to four query heads at a time.
-// Everything is float32 arithmetic; the packed-fp32 instructions are disabled
-// at compile time.
+//  * decode: a wave owns 64 blocks, one per lane; stage-one outputs come from a
+//    small LDS table indexed by two packed codes, the other butterfly stages run in
+//    registers, and the fp16 tile leaves through an XOR-swizzled LDS transpose as
+//    16-byte stores, 1 KB contiguous per instruction.
+//  * q.K: q . (H y) = (H q) . y since H is symmetric, so each query slice is rotated
+//    once per workgroup and the keys' levels enter v_mfma_f32_16x16x32_f16 as fp16
+//    hi / lo pairs read from an LDS table; the decoded key is never formed.
+//  * decode attention: the same scores, an online softmax per 64 rows and P.V on the
+//    matrix cores in the rotated domain, one inverse transform per head at the end
+//    of a second (combine) pass over per-chunk partials.
+//  * interleaved records: LDS-staged 16-byte moves between the planes and the
+//    50 / 34-byte block records.
+//  * the randomised rotation H D flips fp16 sign bits (XOR) where the kernels load
+//    or store values, and the query and the attention output where they enter and
+//    leave.
+// Arithmetic is float32, except the matrix-core operands (fp16 inputs, fp16 hi / lo
+// splits of float values); the packed-fp32 instructions are disabled at compile
+// time.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -191,10 +195,10 @@ __device__ __forceinline__ int64_t cache_block(uint32_t b, uint32_t row_blocks,
     return (int64_t)lh * cache_row_blocks + t0_blocks + r;
 }
 
-// Wave tiles: tile i is x-blocks [64 i, 64 i + 64) (the last one may be short).
-// Encode and decode run persistent waves: wave w handles tiles w, w + W, w + 2W...
-// (W = waves in the grid), prefetching tile i + W while it computes tile i, so
-// HBM traffic and VALU work of different tiles overlap inside every wave.
+// Wave tiles: 32 (encode) or 64 (decode) consecutive blocks (the last one may be
+// short).  Encode and decode run persistent waves: wave w handles tiles w, w + W,
+// w + 2W... (W = waves in the grid), prefetching tile i + W while it computes tile i,
+// so HBM traffic and the ALU work of different tiles overlap inside every wave.
 
 // Encode tiles: 32 blocks per wave (two 16-block column tiles of the matrix-core
 // rotation below); the staged codes of a tile leave as 16-byte stores.
