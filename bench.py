@@ -90,7 +90,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this codec path runs on a single MI355X "
-              "(every block is independent; multi-GPU sharding is not part of this build).",
+              "(every block is independent; a cache sharded over GPUs runs this same path on each "
+              "GPU's shard, launched by its own process).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -287,7 +288,22 @@ def main():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "one_layer_kv_kernels_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_quantization_block_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_quantization_block_amd", "csrc", f)
+                  for f in ("kernels.hip", "internal.h")]
+
+
+def kernel_code_sha() -> str:
+    """First 16 hex digits of the sha256 of the kernels' code (kernels.hip, internal.h):
+    comments removed and
+    every run of whitespace made one space, so an edit of comments or layout alone does
+    not count as a change of the kernels."""
+    import hashlib
+    import re
+    src = "".join(open(f, encoding="utf-8").read() for f in KERNEL_SOURCES)
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    code = tok.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def measured_traffic(kernel: str):
@@ -295,7 +311,6 @@ def measured_traffic(kernel: str):
     committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy of
     known size), or None when the summary does not cover this op or the kernel source
     changed since it was taken."""
-    import hashlib
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = {}
@@ -304,8 +319,7 @@ def measured_traffic(kernel: str):
         if ":" in line:
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != sha or f"{kernel}.fetch_size_kib" not in rec:
+    if rec.get("kernel_code_sha256_16") != kernel_code_sha() or f"{kernel}.fetch_size_kib" not in rec:
         return None
     copy_kib = int(rec["copy_bytes"]) / 1024
     fetch = float(rec[f"{kernel}.fetch_size_kib"]) * copy_kib / float(rec["copy_fetch_size_kib"])

@@ -1700,9 +1700,6 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
 }
 
 
-// Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
-// device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
-// of kAttnDepth units per wave, at most 65535 chunks.
 int launch_pack_records(int bits, const void *codes, const void *norms, int64_t nblocks,
                         void *records, void *stream)
 {
@@ -1733,6 +1730,9 @@ int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *
     return (int)hipGetLastError();
 }
 
+// Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
+// device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
+// of kAttnDepth units per wave, at most 65535 chunks.
 int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
