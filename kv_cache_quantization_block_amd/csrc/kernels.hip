@@ -654,8 +654,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restric
 // (group, block) units whose codes are in flight while the previous ones are
 // scored; a group is the 16 tokens one wave scores at once.
 constexpr int kQkDepth = 8;
-constexpr int kQkHeads = 8;
-constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)   // query heads per pass
+constexpr int kQkHeads = 8;         // query heads per pass
+constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)
 // turbo3: 64 two-value entries of 8 B, kLdsCopies8 copies (conflict-free);
 // turbo2: 256 four-value entries of 16 B, 8 copies (16 B lookups are served 16 lanes
 // per cycle, so lanes l and l + 8 may meet: the full 16 copies would take 64 KB and
@@ -901,7 +901,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     // norm from the lane that holds it; a separate small load per unit would cost the
     // memory pipeline about as much as the unit's codes.
     static_assert(!ONE_BLOCK || kQkDepth * 16 == 128, "two norm loads per batch");
-    auto fetch_norms = [&](uint32_t k, uint32_t &na, uint32_t &nb) {
+    auto fetch_norms = [&](uint32_t k, uint16_t &na, uint16_t &nb) {
         const uint32_t ta = min(first + 16u * k + lane, t_end - 1u);
         const uint32_t tb = min(first + 16u * k + 64u + lane, t_end - 1u);
         na = ld_stream(k_norms + row0 + ta);
@@ -909,7 +909,9 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     };
     uint32_t wn[kQkDepth][LW];
     uint16_t nn[kQkDepth];
-    uint32_t nna = 0, nnb = 0;
+    // (16-bit, widened only where used: a widening right after the load would wait
+    // for it there)
+    uint16_t nna = 0, nnb = 0;
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
         fetch(d, wn[d], nn[d]);
@@ -957,7 +959,60 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     float *const out_s = scores + ((size_t)b * Hq + h0 + sh) * T;
 
     f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (uint32_t k0 = 0; k0 < nunits; k0 += kQkDepth) {
+    uint32_t k0 = 0;
+    if constexpr (ONE_BLOCK) {
+        // Whole batches (128 rows inside the wave's range, 16-byte aligned score
+        // rows): the next batch's loads are unconditional (rows clamped inside the
+        // chunk), every lane stores a 16-byte score line per unit pair (a lane whose
+        // head is past the pass's last one writes that head's line again, with the
+        // same values), and the next batch's codes are taken at the end of the batch.
+        // The loop body then has no branch around a memory operation, and the wait
+        // for the prefetched codes counts exactly the score stores issued after them.
+        const uint32_t nfull = rows16 && first < last ? (last - first) / 128u * kQkDepth : 0u;
+        const uint32_t shf = min(sh, nh - 1u);
+        float *const out_f = scores + ((size_t)b * Hq + h0 + shf) * T;
+        uint32_t wc[kQkDepth][LW];
+        uint16_t nca = nna, ncb = nnb;
+#pragma unroll
+        for (int d = 0; d < kQkDepth; ++d)
+#pragma unroll
+            for (int i = 0; i < LW; ++i)
+                wc[d][i] = wn[d][i];
+        for (; k0 < nfull; k0 += kQkDepth) {
+#pragma unroll
+            for (int d = 0; d < kQkDepth; ++d)
+                fetch(k0 + kQkDepth + d, wn[d], nn[d]);
+            fetch_norms(k0 + kQkDepth, nna, nnb);
+#pragma unroll
+            for (int d = 0; d < kQkDepth; ++d) {
+                const uint16_t nr16 = (uint16_t)__shfl((int)(uint32_t)(d < 4 ? nca : ncb),
+                                                       16 * (d & 3) + (int)n, 64);
+                const f4_t Du = qk_unit<BITS>(A, wc[d], tcopy) *
+                                (float)__builtin_bit_cast(_Float16, nr16);
+                float s0 = Du[0], s1 = Du[1], s2 = Du[2], s3 = Du[3];
+                swap32(s0, s1);
+                swap32(s2, s3);
+                stg[hu * 32 + 16 * (d & 1) + n] = (s0 + s1) * pw_u;
+                stg[(hu + 2) * 32 + 16 * (d & 1) + n] = (s2 + s3) * pw_v;
+                if (d & 1) {
+                    wave_lds_sync();
+                    const float4 sv = *(const float4 *)(stg + shf * 32 + sr);
+                    *(float4 *)(out_f + first + (k0 + d - 1u) * 16u + sr) = sv;
+                    wave_lds_sync();   // the stage is read before the next pair writes it
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < kQkDepth; ++d)
+#pragma unroll
+                for (int i = 0; i < LW; ++i)
+                    wc[d][i] = wn[d][i];
+            nca = nna;
+            ncb = nnb;
+        }
+    }
+    // Remaining units (all of them for D = 256; at most one ragged batch for D = 128,
+    // whose codes are already in wn).
+    for (; k0 < nunits; k0 += kQkDepth) {
         uint32_t wc[kQkDepth][LW];
         uint16_t nc[kQkDepth];
 #pragma unroll
@@ -967,7 +1022,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                 wc[d][i] = wn[d][i];
             nc[d] = nn[d];
         }
-        const uint32_t nca = nna, ncb = nnb;
+        const uint16_t nca = nna, ncb = nnb;
         if (k0 + kQkDepth < nunits) {
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
@@ -985,7 +1040,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             const uint32_t *w = wc[d];
             uint16_t nr16 = nc[d];
             if constexpr (ONE_BLOCK)
-                nr16 = (uint16_t)__shfl((int)(d < 4 ? nca : ncb), 16 * (d & 3) + (int)n, 64);
+                nr16 = (uint16_t)__shfl((int)(uint32_t)(d < 4 ? nca : ncb), 16 * (d & 3) + (int)n, 64);
             const float nf = (float)__builtin_bit_cast(_Float16, nr16);
             const f4_t Du = qk_unit<BITS>(A, w, tcopy);
             if constexpr (ONE_BLOCK)

@@ -184,6 +184,9 @@ def _qk_case(bits, B, Hkv, G, Tc, T, D, seed, q_mul=None, scale=None):
     (1, 2, 5, 20, 17, 1024),     # eight blocks per row
     (1, 1, 2, 24, 21, 2048),     # sixteen blocks per row (largest head_dim, 96 KB of LDS for turbo2)
     (1, 2, 4, 5000, 4999, 128),  # many token chunks and waves, ragged last group
+    (1, 2, 4, 5000, 5000, 128),  # score rows 16-byte aligned: whole 128-row batches, then a ragged one
+    (1, 1, 12, 1000, 1000, 128), # whole batches in passes of eight and four heads
+    (2, 2, 4, 700, 644, 128),    # whole batches with Tc > T, waves past the last row
 ])
 def test_qk_scores(bits, case):
     B, Hkv, G, Tc, T, D = case
