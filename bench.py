@@ -147,11 +147,9 @@ def main():
 
     def step(dom_i=-1, ev=None):
         for i, (_, _, fn) in enumerate(ops):
-            if i == dom_i:
-                ev[0].record(stream)
+            if i == dom_i:   # the launch's own dispatch records start and stop
+                tq.tq_time_next_launch(ev[0], ev[1])
             fn()
-            if i == dom_i:
-                ev[1].record(stream)
 
     # Settle: the GPU ramps its clocks up only after tens of milliseconds of sustained
     # load, so whole steps run untimed for at least SETTLE_S before the W warm-up steps.
@@ -229,10 +227,14 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, wall clock between two device synchronisations; the
-    # dominant kernel's launches are bracketed by HIP events on the launch stream
+    # timed region: K steps, wall clock between two device synchronisations; each
+    # launch of the dominant kernel records HIP events on its stream from its own
+    # dispatch packet (tq_time_next_launch; the events are created by a first record)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):

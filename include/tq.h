@@ -34,7 +34,8 @@
  *
  * Memory and streams: every pointer named "device" is device memory the
  * caller owns (e.g. from torch on ROCm).  The library allocates, frees and
- * synchronises nothing and keeps no per-call state.  stream is a hipStream_t
+ * synchronises nothing and keeps no per-call state (the one exception is the
+ * per-thread timing hook, tq_time_next_launch).  stream is a hipStream_t
  * passed as void* (NULL = the default stream); calls are asynchronous on it
  * and their results are valid once the caller has synchronised that stream.
  *
@@ -188,6 +189,20 @@ int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
                        int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq,
                        float scale, float *out, void *workspace, int64_t workspace_bytes,
                        void *stream);
+
+/* Timing hook: a measurement aid, not an operation of the codec.
+ * The next kernel this thread launches through any tq_* call records its own start
+ * and stop on these events.  The timestamps are those of the kernel's dispatch
+ * packet (hipExtLaunchKernelGGL), as a kernel trace reports them, without the
+ * dispatch latency that events recorded around the call add.  The hook then clears
+ * itself.
+ * start_event, stop_event: hipEvent_t created by the caller with timing enabled,
+ *   passed as void*; either may be NULL (that side is not recorded); both NULL
+ *   clears a pending hook.
+ * A call that launches two kernels (tq_attn_decode) times the first; a call that
+ * returns an error before launching leaves the hook pending.  Per thread; the
+ * library never waits on the events.  Returns TQ_OK. */
+int tq_time_next_launch(void *start_event, void *stop_event);
 
 #ifdef __cplusplus
 }

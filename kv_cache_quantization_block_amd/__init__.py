@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.tq_pack_records.argtypes = [i32, vp, vp, i64, vp, vp]
     L.tq_unpack_records.restype = i32
     L.tq_unpack_records.argtypes = [i32, vp, i64, vp, vp, vp]
+    L.tq_time_next_launch.restype = i32
+    L.tq_time_next_launch.argtypes = [vp, vp]
     for name, plain in (("tq_encode_rot", L.tq_encode), ("tq_decode_rot", L.tq_decode),
                         ("tq_qk_scores_rot", L.tq_qk_scores), ("tq_attn_decode_rot", L.tq_attn_decode)):
         f = getattr(L, name)
@@ -296,6 +298,27 @@ def tq_pack_records(type: int, codes: torch.Tensor, norms: torch.Tensor, records
                                nb, _dev(records, "records", torch.uint8), _stream(stream))
     if rc:
         raise TQError(rc, "tq_pack_records")
+
+
+def _event_handle(e):
+    if e is None:
+        return None
+    if isinstance(e, int):
+        return e
+    h = getattr(e, "cuda_event", 0)      # torch.cuda.Event: its hipEvent_t, once created
+    if not h:
+        raise ValueError("the event has no HIP event yet: record it once first "
+                         "(torch.cuda.Event creates its event at the first record)")
+    return h
+
+
+def tq_time_next_launch(start_event, stop_event) -> None:
+    """Arm the per-thread timing hook: the next kernel launched by a tq_* call records
+    its own start / stop on these events (torch.cuda.Event with timing, already
+    recorded once; raw hipEvent_t ints; or None)."""
+    rc = lib().tq_time_next_launch(_event_handle(start_event), _event_handle(stop_event))
+    if rc:
+        raise TQError(rc, "tq_time_next_launch")
 
 
 def tq_unpack_records(type: int, records: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,

@@ -266,6 +266,12 @@ int tq_unpack_records(int type, const void *records, int64_t nblocks, void *code
                : TQ_OK;
 }
 
+int tq_time_next_launch(void *start_event, void *stop_event)
+{
+    tq::set_next_launch_events(start_event, stop_event);
+    return TQ_OK;
+}
+
 }  // extern "C"
 
 // Shapes of the decode attention call (D = 128); fills the cache blocks of one cache.

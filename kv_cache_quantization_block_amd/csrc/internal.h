@@ -40,6 +40,10 @@ struct Signs {
 
 // Kernel launchers (asynchronous on `stream`).  Each returns 0 on a clean
 // launch and a nonzero HIP error code otherwise.  Shapes are pre-validated.
+// The next kernel launched by this thread records its own start / stop on these
+// hipEvent_t (null: no event); the hook then clears itself.
+void set_next_launch_events(void *start, void *stop);
+
 int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int64_t row_blocks,
                   int64_t cache_row_blocks, int64_t t0_blocks, void *codes, void *norms,
                   void *stream);

@@ -38,6 +38,7 @@
 // Arithmetic is float32, except the matrix-core operands (fp16 inputs, fp16 hi / lo
 // splits of float values); the packed-fp32 instructions are disabled at compile
 // time.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1680,6 +1681,31 @@ inline int grid_for(int64_t nblocks, int tile_blocks, int per_cu)
 
 static bool has_signs(const Signs &sg) { return (sg.w[0] | sg.w[1] | sg.w[2] | sg.w[3]) != 0u; }
 
+// Timing hook: start / stop events for the next kernel this thread launches.
+static thread_local hipEvent_t next_start = nullptr, next_stop = nullptr;
+
+void set_next_launch_events(void *start, void *stop)
+{
+    next_start = (hipEvent_t)start;
+    next_stop = (hipEvent_t)stop;
+}
+
+// Every kernel launch goes through here: a plain launch, or, when the timing hook is
+// set, one whose dispatch packet itself records the start and stop timestamps
+// (hipExtLaunchKernelGGL), after which the hook is cleared.
+template <typename F, typename... Args>
+static void launch_kernel(F kern, dim3 grid, dim3 block, uint32_t smem, hipStream_t s,
+                          Args... args)
+{
+    if (next_start || next_stop) {
+        hipEvent_t a = next_start, b = next_stop;
+        next_start = next_stop = nullptr;
+        hipExtLaunchKernelGGL(kern, grid, block, smem, s, a, b, 0u, args...);
+    } else {
+        hipLaunchKernelGGL(kern, grid, block, smem, s, args...);
+    }
+}
+
 int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int64_t row_blocks,
                   int64_t cache_row_blocks, int64_t t0_blocks, void *codes, void *norms,
                   void *stream)
@@ -1691,9 +1717,9 @@ int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int
     const bool rot = has_signs(sg);
     dim3 grid(grid_for(nblocks, kEncTileBlocks, rot ? per_cu_rot : per_cu)), block(256);
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, s, (const uint8_t *)x, (uint32_t)nblocks,
-                           (uint32_t)row_blocks, cache_row_blocks, t0_blocks, (uint8_t *)codes,
-                           (uint16_t *)norms, *cb, sg);
+        launch_kernel(kern, grid, block, 0, s, (const uint8_t *)x, (uint32_t)nblocks,
+                      (uint32_t)row_blocks, cache_row_blocks, t0_blocks, (uint8_t *)codes,
+                      (uint16_t *)norms, *cb, sg);
     };
     if (bits == 3)
         rot ? launch(encode_kernel<3, true>) : launch(encode_kernel<3, false>);
@@ -1711,9 +1737,9 @@ int launch_decode(int bits, const Signs &sg, const void *codes, const void *norm
     static const int per_cu = groups_per_cu("TQ_DECODE_GROUPS_PER_CU", 2);
     dim3 grid(grid_for(nblocks, kBlocksPerWave, per_cu)), block(256);
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, s, (const uint8_t *)codes, (const uint16_t *)norms,
-                           (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
-                           (uint8_t *)x, *cb, sg);
+        launch_kernel(kern, grid, block, 0, s, (const uint8_t *)codes, (const uint16_t *)norms,
+                      (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
+                      (uint8_t *)x, *cb, sg);
     };
     const bool rot = has_signs(sg);
     if (bits == 3)
@@ -1756,10 +1782,10 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
             if (e != hipSuccess)
                 return (int)e;
         }
-        hipLaunchKernelGGL(kern, grid, block, smem, s, (const uint8_t *)k_codes,
-                           (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,
-                           Tc, (uint32_t)T, (uint32_t)m, (uint32_t)G, (uint32_t)Hq,
-                           (uint32_t)passes, (uint32_t)tpg, scale, *cb, sg);
+        launch_kernel(kern, grid, block, smem, s, (const uint8_t *)k_codes,
+                      (const uint16_t *)k_norms, (const uint16_t *)q, scores, (uint32_t)Hkv,
+                      Tc, (uint32_t)T, (uint32_t)m, (uint32_t)G, (uint32_t)Hq,
+                      (uint32_t)passes, (uint32_t)tpg, scale, *cb, sg);
         return (int)hipGetLastError();
     };
     if (bits == 3)
@@ -1775,11 +1801,11 @@ int launch_pack_records(int bits, const void *codes, const void *norms, int64_t 
     const int64_t tiles = (nblocks + kRecTile - 1) / kRecTile;
     dim3 grid((uint32_t)((tiles + kWavesPerGroup - 1) / kWavesPerGroup)), block(256);
     if (bits == 3)
-        hipLaunchKernelGGL(pack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)codes,
-                           (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
+        launch_kernel(pack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)codes,
+                      (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
     else
-        hipLaunchKernelGGL(pack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)codes,
-                           (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
+        launch_kernel(pack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)codes,
+                      (const uint16_t *)norms, (uint32_t)nblocks, (uint8_t *)records);
     return (int)hipGetLastError();
 }
 
@@ -1790,11 +1816,11 @@ int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *
     const int64_t tiles = (nblocks + kRecTile - 1) / kRecTile;
     dim3 grid((uint32_t)((tiles + kWavesPerGroup - 1) / kWavesPerGroup)), block(256);
     if (bits == 3)
-        hipLaunchKernelGGL(unpack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)records,
-                           (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
+        launch_kernel(unpack_records_kernel<3>, grid, block, 0, s, (const uint8_t *)records,
+                      (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
     else
-        hipLaunchKernelGGL(unpack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)records,
-                           (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
+        launch_kernel(unpack_records_kernel<2>, grid, block, 0, s, (const uint8_t *)records,
+                      (uint32_t)nblocks, (uint8_t *)codes, (uint16_t *)norms);
     return (int)hipGetLastError();
 }
 
@@ -1832,24 +1858,24 @@ int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_no
     const uint32_t nparts = (uint32_t)chunks;
     dim3 grid((uint32_t)(B * Hkv * passes), (uint32_t)chunks), block(256);
     if (bits == 3)
-        hipLaunchKernelGGL((G > 4 ? attn_partial_kernel<3, 2> : attn_partial_kernel<3, 1>), grid,
-                           block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
-                           (const uint8_t *)v_codes, (const uint16_t *)v_norms,
-                           (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
-                           (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                           scale, *cb, sg);
+        launch_kernel((G > 4 ? attn_partial_kernel<3, 2> : attn_partial_kernel<3, 1>), grid,
+                      block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
+                      (const uint8_t *)v_codes, (const uint16_t *)v_norms,
+                      (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
+                      (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
+                      scale, *cb, sg);
     else
-        hipLaunchKernelGGL((G > 4 ? attn_partial_kernel<2, 2> : attn_partial_kernel<2, 1>), grid,
-                           block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
-                           (const uint8_t *)v_codes, (const uint16_t *)v_norms,
-                           (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
-                           (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                           scale, *cb, sg);
+        launch_kernel((G > 4 ? attn_partial_kernel<2, 2> : attn_partial_kernel<2, 1>), grid,
+                      block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
+                      (const uint8_t *)v_codes, (const uint16_t *)v_norms,
+                      (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
+                      (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
+                      scale, *cb, sg);
     int e = (int)hipGetLastError();
     if (e)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
-                       (const float *)work, out, nparts, sg);
+    launch_kernel(attn_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
+                  (const float *)work, out, nparts, sg);
     return (int)hipGetLastError();
 }
 

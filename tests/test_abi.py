@@ -248,3 +248,14 @@ def test_record_validation(L):
     assert u(3, _p(R), 8, _p(C), _p(C + 384 - 2), None) == E_ALIAS      # norms inside the codes
     assert u(3, _p(R), 8, _p(R + 16), _p(N), None) == E_ALIAS
     assert u(3, None, 0, None, None, None) == OK
+
+
+def test_timing_hook_sets_and_clears_without_a_gpu(L):
+    """tq_time_next_launch only stores per-thread state: arming and clearing it needs
+    no device, and the binding refuses a torch event that has no HIP event yet."""
+    import torch
+    assert L.tq_time_next_launch(ctypes.c_void_p(0x1000), None) == OK
+    assert L.tq_time_next_launch(None, None) == OK     # cleared: no launch will touch 0x1000
+    with pytest.raises(ValueError, match="record it once"):
+        tq.tq_time_next_launch(torch.cuda.Event(enable_timing=True), None)
+    tq.tq_time_next_launch(None, None)
