@@ -10,7 +10,6 @@ namespace tq {
 constexpr int kBlock = 128;          // values per block
 constexpr int kWave = 64;            // gfx950 wavefront size
 constexpr int kWavesPerGroup = 4;    // 256-thread workgroups
-constexpr int kBlocksPerWave = 64;   // encode / decode: one block per lane
 
 // float32 constants of one cache type, produced on the host from the N(0,1)
 // Lloyd-Max conditions and handed to the kernels by value.

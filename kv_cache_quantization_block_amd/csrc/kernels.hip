@@ -20,9 +20,10 @@
 //    2^b/2 + g(t), whose floor is the code; the last FMA adds 2^23 under
 //    round-toward-minus-infinity, which leaves the floor in the low mantissa
 //    bits, and eight codes are then packed by seven shift-adds.
-//  * decode: a wave owns 64 blocks, one per lane; stage-one outputs come from a
-//    small LDS table indexed by two packed codes, the other butterfly stages run in
-//    registers, and the fp16 tile leaves through an XOR-swizzled LDS transpose as
+//  * decode: the same factorisation run backwards.  A wave owns 32 blocks; the
+//    levels, looked up two codes at a time in a small LDS table as fp16 hi / lo
+//    pairs, enter the H_32 products as the B operand, H_4 and the rescale run in
+//    registers, and the fp16 output leaves through an XOR-swizzled LDS stage as
 //    16-byte stores, 1 KB contiguous per instruction.
 //  * q.K: q . (H y) = (H q) . y since H is symmetric, so each query slice is rotated
 //    once per workgroup and the keys' levels enter v_mfma_f32_16x16x32_f16 as fp16
@@ -53,11 +54,9 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));   // a matrix-core fp16 operand
 typedef float f4_t __attribute__((ext_vector_type(4)));      // a 16 x 16 product's four rows
 
-constexpr int kTileBytes = kBlocksPerWave * kBlock * 2;   // 16 KB of fp16 per wave
-
-// Wave-private LDS tile of 64 blocks x 256 B.  Chunk c (16 B) of block b sits
-// at b*256 + ((c ^ (b & 15)) * 16): a row of 16 chunks (coalesced side) and a
-// column of 8 consecutive blocks (per-lane side) both touch distinct banks.
+// Wave-private LDS tile of fp16 blocks, 256 B each.  Chunk c (16 B) of block b sits
+// at b*256 + ((c ^ (b & 15)) * 16): 16 lanes writing one chunk of 16 consecutive
+// blocks, and 16 lanes reading the 16 chunks of one block, both touch distinct banks.
 __device__ __forceinline__ uint32_t swz(uint32_t blk, uint32_t chunk)
 {
     return blk * 256u + ((chunk ^ (blk & 15u)) << 4);
@@ -67,6 +66,18 @@ __device__ __forceinline__ uint32_t swz(uint32_t blk, uint32_t chunk)
 // bit-casting an element of an ext_vector (w.y) directly reads element 0 with
 // this compiler, so vector elements always go through a scalar first.
 __device__ __forceinline__ h2_t as_h2(uint32_t word) { return __builtin_bit_cast(h2_t, word); }
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
+{
+    return __builtin_bit_cast(uint32_t, h2_t{a, b});
+}
+
+// x = hi + lo with hi = fp16(x), lo = fp16(x - hi) (x - hi is exact in float).
+__device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
+{
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
 
 // Streaming global accesses.  Each call reads its inputs (fp16 K/V, codes, norms)
 // exactly once, so those loads carry the non-temporal hint: they do not allocate
@@ -171,22 +182,6 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// In-register butterflies of the stages with span h in [H0, H1).
-template <int H0, int H1 = kBlock>
-__device__ __forceinline__ void fwht_from(float (&u)[kBlock])
-{
-#pragma unroll
-    for (int h = H0; h < H1; h <<= 1)
-#pragma unroll
-        for (int i = 0; i < kBlock; i += 2 * h)
-#pragma unroll
-            for (int j = i; j < i + h; ++j) {
-                float a = u[j], b = u[j + h];
-                u[j] = a + b;
-                u[j + h] = a - b;
-            }
-}
-
 // Cache block of x-block b: x row (lh, t) -> cache row (lh, t0 + t).
 __device__ __forceinline__ int64_t cache_block(uint32_t b, uint32_t row_blocks,
                                                int64_t cache_row_blocks, int64_t t0_blocks)
@@ -196,13 +191,10 @@ __device__ __forceinline__ int64_t cache_block(uint32_t b, uint32_t row_blocks,
     return (int64_t)lh * cache_row_blocks + t0_blocks + r;
 }
 
-// Wave tiles: 32 (encode) or 64 (decode) consecutive blocks (the last one may be
-// short).  Encode and decode run persistent waves: wave w handles tiles w, w + W,
-// w + 2W... (W = waves in the grid), prefetching tile i + W while it computes tile i,
-// so HBM traffic and the ALU work of different tiles overlap inside every wave.
-
-// Encode tiles: 32 blocks per wave (two 16-block column tiles of the matrix-core
-// rotation below); the staged codes of a tile leave as 16-byte stores.
+// Codec wave tiles: 32 consecutive blocks (the last one may be short), two 16-block
+// column tiles of the matrix-core rotation (encode and decode).  Wave w handles tiles
+// w, w + W, w + 2W... (W = waves in the grid); the grid normally gives every wave
+// one tile (an encode wave with several prefetches tile i + W while it computes i).
 constexpr int kEncTileBlocks = 32;
 
 // (upper 32 lanes of a) <-> (lower 32 lanes of b), returned as the new (a, b).
@@ -459,165 +451,203 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
 }
 
 // ---------------------------------------------------------------- decode
-
-// This lane's block of the cache: packed codes and the fp16 norm (zeros past nb).
-template <int BITS>
-__device__ __forceinline__ void load_codes(uint32_t (&W)[4 * BITS], uint16_t &N,
-                                           const uint8_t *__restrict__ codes,
-                                           const uint16_t *__restrict__ norms, uint32_t b,
-                                           uint32_t nblocks, uint32_t row_blocks,
-                                           int64_t cache_row_blocks, int64_t t0_blocks)
-{
-    if (b < nblocks) {
-        const int64_t src = cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
-        const u4_t *in = (const u4_t *)(codes + src * (16 * BITS));
-#pragma unroll
-        for (int k = 0; k < BITS; ++k) {
-            const u4_t c = ld_stream(in + k);
-            W[4 * k] = c.x;
-            W[4 * k + 1] = c.y;
-            W[4 * k + 2] = c.z;
-            W[4 * k + 3] = c.w;
-        }
-        N = ld_stream(norms + src);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4 * BITS; ++k)
-            W[k] = 0u;
-        N = 0;
-    }
-}
-
-// Writes a decoded tile from its LDS image: 1 KB contiguous 16-byte stores.
-template <bool ROT>
-__device__ __forceinline__ void store_dec_tile(const uint8_t *lds, uint32_t lane, uint32_t b0,
-                                               uint32_t nb, uint8_t *__restrict__ x, u4_t smask)
-{
-    uint8_t *dst = x + (size_t)b0 * (kBlock * 2) + lane * 16;
-    if (nb == kBlocksPerWave) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const u4_t r = *(const u4_t *)(lds + swz(4 * k + (lane >> 4), lane & 15u));
-            *(u4_t *)(dst + k * 1024) = ROT ? r ^ smask : r;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t blk = 4 * k + (lane >> 4);
-            const u4_t r = *(const u4_t *)(lds + swz(blk, lane & 15u));
-            if (blk < nb)
-                *(u4_t *)(dst + k * 1024) = ROT ? r ^ smask : r;
-        }
-    }
-}
-
-// ROT: x_hat = D (n16 / 128) H y: the fp16 tile's 16-byte stores always hold the same
-// eight positions of a block (chunk lane % 16), so D is one XOR per packed pair.
+//
+// x_hat = (n16 / 128) H y with H = H4 (x) H32 over p = 32 g + q, as in the encoder:
+// v_g'[q] = sum_q' H32[q][q'] y[32 g' + q'] on v_mfma_f32_16x16x32_f16, then two
+// butterfly stages over g' in registers with the rescale folded into the second.
+// The levels enter as fp16 parts yh = fp16(y), yl = fp16(y - yh), two products each:
+// yh + yl carries y to about 2^-22, the +-1 products are exact and the sums fp32.
+//
+// A wave takes 32 blocks as two 16-block column tiles; lane (G = lane / 16, n) takes
+// block 16 c + n.  Its B operand for g' holds the levels of positions 32 g' + 8 G ..
+// + 7: eight codes, one 24 / 16-bit field of the packed block (bytes 12 g' + 3 G /
+// 8 g' + 2 G), as four lookups of two-code (yh pair, yl pair) entries.  After the
+// butterflies it holds positions 32 g + 8 G .. + 7 for g = 0..3: four 16-byte stores.
+// The codes arrive as whole 16-byte chunks (one instruction reads 16 blocks) through
+// a small LDS stage per wave.  The grid gives every wave one tile.
 template <int BITS, bool ROT>
-__global__ __launch_bounds__(256, 2) void decode_kernel(const uint8_t *__restrict__ codes,
-                                                        const uint16_t *__restrict__ norms,
-                                                        uint32_t nblocks, uint32_t row_blocks,
-                                                        int64_t cache_row_blocks,
-                                                        int64_t t0_blocks,
-                                                        uint8_t *__restrict__ x, Codebook cb,
-                                                        Signs sg)
+__global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restrict__ codes,
+                                                            const uint16_t *__restrict__ norms,
+                                                            uint32_t nblocks, uint32_t row_blocks,
+                                                            int64_t cache_row_blocks,
+                                                            int64_t t0_blocks,
+                                                            uint8_t *__restrict__ x, Codebook cb,
+                                                            Signs sg)
 {
-    // Entry e (2 b code bits = two codes, the first in the low bits) -> stage-one
-    // outputs (y0 + y1, y0 - y1); 64 entries for turbo3, 16 for turbo2, each
-    // replicated kLdsCopies8 times so that the 32 lanes of one LDS cycle never
-    // collide (copy c of entry e at (e * 32 + c) * 8, lane l reads copy l % 32).
-    constexpr int NE = 1 << (2 * BITS);
-    constexpr int kTableBytes = NE * kLdsCopies8 * 8;
-    // one LDS buffer, the table first
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kTableBytes + kWavesPerGroup * kTileBytes];
-    // the levels pass through the first tile's bytes, which no wave uses before the
-    // barrier that ends the table build (two 80 KB groups fill a CU's 160 KB exactly)
-    float *lv = (float *)(smem + kTableBytes);
+    constexpr int FB = 2 * BITS;   // index bits of a two-code entry
+    constexpr int NE = 1 << FB;
+    constexpr int CB = 16 * BITS;  // code bytes per block
+    // entry e (first code in the low bits) -> (yh0 | yh1 << 16, yl0 | yl1 << 16),
+    // kLdsCopies8 copies: copy c of entry e at (32 e + c) * 8, lane l reads copy l % 32
+    __shared__ __attribute__((aligned(16))) uint8_t table[NE * kLdsCopies8 * 8];
+    // per wave: the tile's codes, then (once every field is in registers) one column
+    // tile's fp16 output at a time, block b at b * 256 with 16-byte chunk k at
+    // (k ^ b) * 16
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWavesPerGroup][16 * kBlock * 2];
+    static_assert(kEncTileBlocks * CB <= 16 * kBlock * 2, "the codes fit the output stage");
+    __shared__ float lv[8];
+    __shared__ uint2 ent_s[NE];
     levels_to_lds(lv, cb);
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += blockDim.x) {
-        const uint32_t e = i / kLdsCopies8;
-        const float y0 = lv[e & ((1u << BITS) - 1u)], y1 = lv[e >> BITS];
-        *(float2 *)(smem + i * 8) = float2{y0 + y1, y0 - y1};
+    // each entry is converted once (thread e), then copied: consecutive lanes write
+    // consecutive copies, which meets every bank once
+    if (threadIdx.x < (uint32_t)NE) {
+        const uint32_t e = threadIdx.x;
+        _Float16 a0, c0, a1, c1;
+        split_f16(lv[e & ((1u << BITS) - 1u)], a0, c0);
+        split_f16(lv[e >> BITS], a1, c1);
+        ent_s[e] = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
     }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += blockDim.x)
+        *(uint2 *)(table + i * 8) = ent_s[i / kLdsCopies8];
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)smem + (lane % kLdsCopies8) * 8;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar
-    const uint32_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n = lane & 15u, G = lane >> 4;
+    const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
+    // cache position of block b: b itself when the cache rows hold exactly the
+    // decoded rows (no division)
+    const bool contig = cache_row_blocks == (int64_t)row_blocks && t0_blocks == 0;
+    auto src_of = [&](uint32_t b) -> int64_t {
+        if (contig)
+            return (int64_t)b;
+        return cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
+    };
     const uint32_t stride = gridDim.x * kWavesPerGroup;
     uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
     if (tile >= ntiles)
         return;
-    uint8_t *lds = smem + kTableBytes + wave * kTileBytes;
-    constexpr int NW = 4 * BITS;
-    const u4_t smask = ROT ? sign_mask_chunk(sg, lane & 15u) : u4_t{0, 0, 0, 0};
 
-    // Per iteration (tile i): take tile i's codes (prefetched), write out tile i-1
-    // from LDS, issue the loads of tile i+1, then compute tile i into LDS.  Stores
-    // and loads are both issued before the compute, so the wave's next wait finds
-    // them complete.
-    uint32_t W[NW];
-    uint16_t N;
-    load_codes<BITS>(W, N, codes, norms, tile * kBlocksPerWave + lane, nblocks, row_blocks,
-                     cache_row_blocks, t0_blocks);
-    uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in LDS
-    for (;;) {
-        const uint32_t b0 = tile * kBlocksPerWave;
-        const uint32_t nb = min(nblocks - b0, (uint32_t)kBlocksPerWave);
-        uint32_t w[NW];
+    // A operands, as in the encoder: row tile r, lane row n -> H32 row
+    // q = 8 (n / 4) + 4 r + n % 4, k-slots 8 G + s: (-1)^popcount(q & k) as fp16
+    h8_t A[2];
 #pragma unroll
-        for (int k = 0; k < NW; ++k)
-            w[k] = W[k];
-        const float scale = (float)__builtin_bit_cast(_Float16, N) * (1.0f / 128.0f);
-        if (pnb)
-            store_dec_tile<ROT>(lds, lane, pb0, pnb, x, smask);
-        const uint32_t next = tile + stride;
-        if (next < ntiles)
-            load_codes<BITS>(W, N, codes, norms, next * kBlocksPerWave + lane, nblocks,
-                             row_blocks, cache_row_blocks, t0_blocks);
-
-        float u[kBlock];
+    for (int r = 0; r < 2; ++r) {
+        const uint32_t q = 8u * (n >> 2) + 4u * r + (n & 3u);
+        uint32_t w[4];
 #pragma unroll
-        for (int p = 0; p < 64; ++p) {
-            constexpr int FB = 2 * BITS;   // index bits: two codes
-            const int bit = FB * p, wi = bit >> 5, sh = bit & 31;
-            const uint32_t e = sh <= 32 - FB ? __builtin_amdgcn_ubfe(w[wi], sh, FB)
-                                             : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & (NE - 1u);
-            const uint64_t t = lds_load<uint64_t>(lshl_add<8>(e, tcopy));
-            u[2 * p] = __builtin_bit_cast(float, (uint32_t)t);
-            u[2 * p + 1] = __builtin_bit_cast(float, (uint32_t)(t >> 32));
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const uint32_t k0 = 8u * G + 2u * s2;
+            const uint32_t h0 = (__builtin_popcount(q & k0) & 1u) ? 0xBC00u : 0x3C00u;
+            const uint32_t h1 = (__builtin_popcount(q & (k0 + 1u)) & 1u) ? 0xBC00u : 0x3C00u;
+            w[s2] = h0 | (h1 << 16);
         }
-        fwht_from<2, 64>(u);
-        // last stage with the rescale by n16/128 folded in: (a +- b) s = a s +- b s
+        A[r] = __builtin_bit_cast(h8_t, u4_t{w[0], w[1], w[2], w[3]});
+    }
+    // randomised rotation: the lane's output chunk g is chunk 4 g + G of its block
+    u4_t smask[4];
 #pragma unroll
-        for (int j = 0; j < 64; ++j) {
-            const float as = u[j] * scale, bj = u[j + 64];
-            u[j] = __builtin_fmaf(bj, scale, as);
-            u[j + 64] = __builtin_fmaf(-bj, scale, as);
-        }
+    for (int g = 0; g < 4; ++g)
+        smask[g] = ROT ? sign_mask_chunk(sg, 4u * g + G) : u4_t{0, 0, 0, 0};
+    const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)table + (lane % kLdsCopies8) * 8;
+    // the wave's codes stage: block 16 c + n of the tile at (16 c + n) * 16 BITS
+    uint8_t *stage = stage_all[wave];
+    // turbo3: the field of g' starts at byte 12 g' + 3 G = dword 3 g' + (3 G) / 4,
+    // bit 8 ((3 G) % 4); it spills into the next dword only for G = 1, 2 (lane groups
+    // 0 and 3 read their one dword twice, which keeps G = 3, g' = 3 inside the block)
+    const uint32_t fdw = (3u * G) >> 2, fsh = 8u * ((3u * G) & 3u), fhi = fsh > 8u ? 1u : 0u;
 
-        // round to fp16 (nearest even) into the LDS tile (block per lane, swizzled)
-        wave_lds_sync();   // the previous tile's rows have been read out
+    for (; tile < ntiles; tile += stride) {
+        const uint32_t b0 = tile * kEncTileBlocks;
+        const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
+        // loads: lane (G, n), G < BITS, takes 16-byte chunk G of block 16 c + n (one
+        // instruction covers 16 whole blocks, contiguous when the cache is); lanes past
+        // nb read the tile's last block
+        u4_t C[2];
+        uint16_t N16[2];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            uint32_t o[4];
+        for (int c = 0; c < 2; ++c) {
+            const int64_t src = src_of(b0 + min(16u * c + n, nb - 1u));
+            C[c] = G < (uint32_t)BITS ? ld_stream((const u4_t *)(codes + src * CB) + G)
+                                      : u4_t{0, 0, 0, 0};
+            N16[c] = ld_stream(norms + src);
+        }
+        wave_lds_sync();   // the previous tile's stage reads are done
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            if (G < (uint32_t)BITS)
+                *(u4_t *)(stage + (16u * c + n) * CB + 16u * G) = C[c];
+        wave_lds_sync();
+        uint32_t F[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint8_t *blk = stage + (16u * c + n) * CB;
+#pragma unroll
+            for (int gp = 0; gp < 4; ++gp) {
+                if constexpr (BITS == 3) {
+                    const uint32_t *p = (const uint32_t *)blk + 3 * gp + fdw;
+                    F[c][gp] = __builtin_amdgcn_alignbit(p[fhi], p[0], fsh);
+                } else {
+                    F[c][gp] = ((const uint16_t *)blk)[4 * gp + G];
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            f4_t D[4][2];
+#pragma unroll
+            for (int gp = 0; gp < 4; ++gp) {
+                uint32_t bh[4], bl[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e = __builtin_amdgcn_ubfe(F[c][gp], FB * j, FB);
+                    const uint64_t t = lds_load<uint64_t>(lshl_add<8>(e, tcopy));
+                    bh[j] = (uint32_t)t;
+                    bl[j] = (uint32_t)(t >> 32);
+                }
+                const h8_t Bh = __builtin_bit_cast(h8_t, u4_t{bh[0], bh[1], bh[2], bh[3]});
+                const h8_t Bl = __builtin_bit_cast(h8_t, u4_t{bl[0], bl[1], bl[2], bl[3]});
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    D[gp][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A[r], Bh, f4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    D[gp][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r], Bl, D[gp][r], 0, 0, 0);
+                }
+            }
+            // u[32 g + 8 G + 4 r + j] = (n16 / 128) sum_g' H4[g][g'] D[g'][r][j]
+            const float s = (float)__builtin_bit_cast(_Float16, N16[c]) * (1.0f / 128.0f);
+            float u[4][8];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = D[0][r][j], v1 = D[1][r][j], v2 = D[2][r][j], v3 = D[3][r][j];
+                    const float a0 = v0 + v1, a1 = v0 - v1, a2 = v2 + v3, a3 = v2 - v3;
+                    const float as0 = a0 * s, as1 = a1 * s;
+                    u[0][4 * r + j] = __builtin_fmaf(a2, s, as0);
+                    u[1][4 * r + j] = __builtin_fmaf(a3, s, as1);
+                    u[2][4 * r + j] = __builtin_fmaf(-a2, s, as0);
+                    u[3][4 * r + j] = __builtin_fmaf(-a3, s, as1);
+                }
+            // every lane's fields (c = 0) or the previous column tile's rows (c = 1)
+            // have been read: the stage takes this column tile's output
+            wave_lds_sync();
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    h2_t hv = {(_Float16)u[g][2 * k], (_Float16)u[g][2 * k + 1]};
+                    o[k] = __builtin_bit_cast(uint32_t, hv);
+                }
+                const u4_t ov = u4_t{o[0], o[1], o[2], o[3]};
+                *(u4_t *)(stage + swz(n, 4u * g + G)) = ROT ? ov ^ smask[g] : ov;
+            }
+            // the column tile leaves as 1 KB-contiguous stores: lane l writes chunk
+            // l % 16 of its block 4 k + l / 16
+            wave_lds_sync();
+            uint8_t *dst = x + (size_t)(b0 + 16u * c) * (kBlock * 2) + lane * 16u;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                h2_t hv = {(_Float16)u[8 * c + 2 * k], (_Float16)u[8 * c + 2 * k + 1]};
-                o[k] = __builtin_bit_cast(uint32_t, hv);
+                const uint32_t blk = 4u * k + (lane >> 4);
+                const u4_t r = *(const u4_t *)(stage + swz(blk, lane & 15u));
+                if (16u * c + blk < nb)
+                    *(u4_t *)(dst + k * 1024) = r;
             }
-            *(u4_t *)(lds + swz(lane, c)) = u4_t{o[0], o[1], o[2], o[3]};
         }
-        wave_lds_sync();
-        pb0 = b0;
-        pnb = nb;
-        tile = next;
-        if (tile >= ntiles)
-            break;
     }
-    store_dec_tile<ROT>(lds, lane, pb0, pnb, x, smask);
 }
 
 // ---------------------------------------------------------------- q.K scores
@@ -668,17 +698,7 @@ inline size_t qk_smem_bytes(int bits, int64_t m)
     return (size_t)qk_table_bytes(bits) + (size_t)m * 16 * kBlock * 2 + kQkHeads * 4;
 }
 
-__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
-{
-    return __builtin_bit_cast(uint32_t, h2_t{a, b});
-}
 
-// x = hi + lo with hi = fp16(x), lo = fp16(x - hi) (x - hi is exact in float).
-__device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
-{
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
-}
 
 // x as packed fp16 (hi, lo): hi = fp16(x), lo = fp16(x - hi) rounded toward zero (hi
 // is exact in fp16, so the truncating pack keeps it).
@@ -725,6 +745,7 @@ __device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv)
         }
     }
 }
+
 
 // Query operands.  Wave w prepares heads w and w + 4 of the pass (h0 .. h0 + nh - 1):
 // rotates every 128-slice (lane l holds positions l and 64 + l; span 64 in-lane, spans
@@ -1654,9 +1675,9 @@ int cu_count()
 //     gain 3-7 %, one layer is unchanged).  The randomised-rotation variant keeps
 //     a persistent grid of two groups per CU: its sign masks take it to 138-142
 //     VGPRs, three waves per SIMD, where one tile per wave runs 13 % slower.
-//   decode: two groups per CU, persistent (2 x 80 KB of LDS, 207-211 VGPRs): every
-//     wave prefetches its next tile's codes, and more groups queued behind the
-//     resident ones slow the one-layer decode (32 -> 37 us at eight per CU).
+//   decode: no cap either, one 32-block tile per wave (82-108 VGPRs and 20 / 33 KB of
+//     LDS allow four to six groups per CU); caps of 5, 10 or 20 groups per CU
+//     measured slower on 8- to 48-layer caches.
 int groups_per_cu(const char *env, int dflt)
 {
     const char *e = getenv(env);
@@ -1734,8 +1755,8 @@ int launch_decode(int bits, const Signs &sg, const void *codes, const void *norm
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
-    static const int per_cu = groups_per_cu("TQ_DECODE_GROUPS_PER_CU", 2);
-    dim3 grid(grid_for(nblocks, kBlocksPerWave, per_cu)), block(256);
+    static const int per_cu = groups_per_cu("TQ_DECODE_GROUPS_PER_CU", 0);
+    dim3 grid(grid_for(nblocks, kEncTileBlocks, per_cu)), block(256);
     auto launch = [&](auto kern) {
         launch_kernel(kern, grid, block, 0, s, (const uint8_t *)codes, (const uint16_t *)norms,
                       (uint32_t)nblocks, (uint32_t)row_blocks, cache_row_blocks, t0_blocks,
