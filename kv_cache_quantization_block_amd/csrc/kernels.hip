@@ -723,27 +723,37 @@ struct QkTable {
 
 // Fills the table of (yh, yl) pairs in the B order: entry e holds the values of codes
 // e & 7, e >> 3 (turbo3) or (e >> 2 k) & 3, k = 0..3 (turbo2).  Whole workgroup; lv
-// are the levels, already in LDS.
+// are the levels, already in LDS.  Each entry is converted once, into `scratch` (NE *
+// EB bytes of LDS the caller does not use until after this call), then copied with
+// consecutive lanes writing consecutive copies; ends with a barrier.
 template <int BITS>
-__device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv)
+__device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv, uint8_t *scratch)
 {
     using Tb = QkTable<BITS>;
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(Tb::NE * Tb::NC); i += blockDim.x) {
-        const uint32_t e = i / Tb::NC;
+    static_assert(Tb::NE * Tb::EB <= 16 * kBlock * 2, "the entries fit one block's query operands");
+    for (uint32_t e = threadIdx.x; e < (uint32_t)Tb::NE; e += blockDim.x) {
         if constexpr (BITS == 3) {
             _Float16 a0, a1, c0, c1;
             split_f16(lv[e & 7], a0, c0);
             split_f16(lv[e >> 3], a1, c1);
-            *(uint2 *)(table + i * Tb::EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
+            *(uint2 *)(scratch + e * Tb::EB) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         } else {
             _Float16 a[4], c[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 split_f16(lv[(e >> (2 * k)) & 3], a[k], c[k]);
-            *(uint4 *)(table + i * Tb::EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
-                                                    pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
+            *(uint4 *)(scratch + e * Tb::EB) = uint4{pack_h2(a[0], a[1]), pack_h2(c[0], c[1]),
+                                                      pack_h2(a[2], a[3]), pack_h2(c[2], c[3])};
         }
     }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(Tb::NE * Tb::NC); i += blockDim.x) {
+        if constexpr (BITS == 3)
+            *(uint2 *)(table + i * Tb::EB) = *(const uint2 *)(scratch + (i / Tb::NC) * Tb::EB);
+        else
+            *(uint4 *)(table + i * Tb::EB) = *(const uint4 *)(scratch + (i / Tb::NC) * Tb::EB);
+    }
+    __syncthreads();
 }
 
 
@@ -943,7 +953,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     __shared__ float lv[8];
     levels_to_lds(lv, cb);
     __syncthreads();
-    qk_fill_table<BITS>(table, lv);
+    qk_fill_table<BITS>(table, lv, (uint8_t *)qa);   // qa is written only below
 
     qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg);
     __syncthreads();
@@ -1258,7 +1268,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     // tables and query operands
     levels_to_lds(lv, cb);
     __syncthreads();
-    qk_fill_table<BITS>(ktable, lv);
+    qk_fill_table<BITS>(ktable, lv, (uint8_t *)qa);   // qa is written only below
     if constexpr (BITS == 2) {
         for (uint32_t i = threadIdx.x; i < 16u * kLdsCopies8; i += blockDim.x) {
             const uint32_t e = i / kLdsCopies8;
