@@ -244,9 +244,12 @@ __device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t la
 {
     constexpr int GW = BITS, GB = 4 * BITS, CB = 16 * BITS;
     const uint32_t blk = lane & 31u, half = lane >> 5;
-    const int64_t dst0 = cache_block(b0, row_blocks, cache_row_blocks, t0_blocks);
-    const int64_t dstl = cache_block(b0 + nb - 1, row_blocks, cache_row_blocks, t0_blocks);
-    if (dstl - dst0 == (int64_t)nb - 1) {
+    // consecutive cache blocks: always when the cache rows hold exactly the encoded
+    // rows (no division needed), else when the tile stays inside one cache row
+    const bool contig = cache_row_blocks == (int64_t)row_blocks && t0_blocks == 0;
+    const int64_t dst0 = contig ? (int64_t)b0 : cache_block(b0, row_blocks, cache_row_blocks, t0_blocks);
+    if (contig ||
+        cache_block(b0 + nb - 1, row_blocks, cache_row_blocks, t0_blocks) - dst0 == (int64_t)nb - 1) {
         uint8_t *gdst = codes + dst0 * CB;
         const uint32_t nchunks = nb * BITS;   // 16-byte chunks of the tile's codes
 #pragma unroll
@@ -336,16 +339,17 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
         smask[gp] = ROT ? sign_mask_chunk(sg, 4u * gp + G) : u4_t{0, 0, 0, 0};
 
     // loads of column tile c of a tile: R[c][g'] = values 32 g' + 8 G .. + 7 of block
-    // b0 + 16 c + n (zeros past the tile's blocks)
+    // b0 + 16 c + n; lanes past the tile's blocks read its last block (their codes and
+    // norms are never stored), so every load is unconditional
     u4_t R[2][4];
     auto load_col = [&](uint32_t t, int c) {
         const uint32_t b0 = t * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
-        const uint32_t b = 16u * c + n;
+        const uint32_t b = min(16u * c + n, nb - 1u);
         const u4_t *src = (const u4_t *)(x + ((size_t)b0 + b) * (kBlock * 2) + 16u * G);
 #pragma unroll
         for (int gp = 0; gp < 4; ++gp)
-            R[c][gp] = b < nb ? ld_stream(src + 4 * gp) : u4_t{0, 0, 0, 0};
+            R[c][gp] = ld_stream(src + 4 * gp);
     };
     load_col(tile, 0);
     load_col(tile, 1);
