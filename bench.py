@@ -254,6 +254,7 @@ def main():
 
     dstep = decode_step(tq, gen, dev, stream) if not args.no_decode_step else None
     bw_cfgs = bandwidth_configs(tq, gen, dev, stream) if not args.no_large else None
+    copy_ctx = copy_bandwidth(dev, stream)
 
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -285,6 +286,7 @@ def main():
         "records": records,
         "decode_step": dstep,
         "bandwidth_configs": bw_cfgs,
+        "copy_context": copy_ctx,
     }
     print(json.dumps(out))
 
@@ -388,6 +390,29 @@ def decode_step(tq, gen, dev, stream, reps=20):
     del kc, kn, vc, vn, scores, attn, ws
     torch.cuda.empty_cache()
     return out
+
+
+def copy_bandwidth(dev, stream, nbytes=512 << 20, reps=10):
+    """Context for the roofline: what a plain device-to-device copy of 512 MiB (torch's
+    copy kernel, read + write counted) reaches on this GPU, HIP events around `reps`
+    back-to-back copies after three untimed ones."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"what": "device-to-device copy, 512 MiB read + 512 MiB written", "us": round(us, 1),
+            "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bandwidth_configs(tq, gen, dev, stream, reps=10):
