@@ -2,7 +2,7 @@
 
 Every case feeds the same fp16 bytes to the library (through the C ABI via the
 Python binding) and to the oracle, then compares element by element under the
-rules in _parity.py.  Sizes span several 64-block wave tiles with ragged tails.
+rules in _parity.py.  Sizes span several 32-block wave tiles with ragged tails.
 """
 import math
 
