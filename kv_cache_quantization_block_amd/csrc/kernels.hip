@@ -316,6 +316,21 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
         return;
     uint8_t *stage = stage_all[wave];
 
+    // loads of column tile c of a tile: R[c][g'] = values 32 g' + 8 G .. + 7 of block
+    // b0 + 16 c + n; lanes past the tile's blocks read its last block (their codes and
+    // norms are never stored), so every load is unconditional
+    u4_t R[2][4];
+    auto load_col = [&](uint32_t t, int c) {
+        const uint32_t b0 = t * kEncTileBlocks;
+        const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
+        const uint32_t b = min(16u * c + n, nb - 1u);
+        const u4_t *src = (const u4_t *)(x + ((size_t)b0 + b) * (kBlock * 2) + 16u * G);
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp)
+            R[c][gp] = ld_stream(src + 4 * gp);
+    };
+    load_col(tile, 0);   // the first tile's loads go out before the operand set-up
+    load_col(tile, 1);
     // A operands: row tile r, lane row n -> H_32 row q = 8 (n / 4) + 4 r + n % 4, k-slots
     // 8 G + s: +-1 as fp16 (sign bit of (-1)^popcount(q & k))
     h8_t A[2];
@@ -338,21 +353,6 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
     for (int gp = 0; gp < 4; ++gp)
         smask[gp] = ROT ? sign_mask_chunk(sg, 4u * gp + G) : u4_t{0, 0, 0, 0};
 
-    // loads of column tile c of a tile: R[c][g'] = values 32 g' + 8 G .. + 7 of block
-    // b0 + 16 c + n; lanes past the tile's blocks read its last block (their codes and
-    // norms are never stored), so every load is unconditional
-    u4_t R[2][4];
-    auto load_col = [&](uint32_t t, int c) {
-        const uint32_t b0 = t * kEncTileBlocks;
-        const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
-        const uint32_t b = min(16u * c + n, nb - 1u);
-        const u4_t *src = (const u4_t *)(x + ((size_t)b0 + b) * (kBlock * 2) + 16u * G);
-#pragma unroll
-        for (int gp = 0; gp < 4; ++gp)
-            R[c][gp] = ld_stream(src + 4 * gp);
-    };
-    load_col(tile, 0);
-    load_col(tile, 1);
     uint32_t pb0 = 0, pnb = 0;   // the finished tile waiting in `stage`
     uint16_t pn16 = 0;
     for (;;) {
