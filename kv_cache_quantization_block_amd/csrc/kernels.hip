@@ -557,15 +557,15 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
         const uint32_t b0 = tile * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
         // loads: lane (G, n), G < BITS, takes 16-byte chunk G of block 16 c + n (one
-        // instruction covers 16 whole blocks, contiguous when the cache is); lanes past
-        // nb read the tile's last block
+        // instruction covers 16 whole blocks, contiguous when the cache is); lanes
+        // G >= BITS repeat chunk BITS - 1 (same addresses) and lanes past nb read the
+        // tile's last block, so every load is unconditional
         u4_t C[2];
         uint16_t N16[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int64_t src = src_of(b0 + min(16u * c + n, nb - 1u));
-            C[c] = G < (uint32_t)BITS ? ld_stream((const u4_t *)(codes + src * CB) + G)
-                                      : u4_t{0, 0, 0, 0};
+            C[c] = ld_stream((const u4_t *)(codes + src * CB) + min(G, (uint32_t)BITS - 1u));
             N16[c] = ld_stream(norms + src);
         }
         wave_lds_sync();   // the previous tile's stage reads are done
