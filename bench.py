@@ -419,8 +419,9 @@ def bandwidth_configs(tq, gen, dev, stream, reps=10):
     """Encode then decode of two whole caches, the sizes where launch ramp and tail
     stop mattering: a 14B-shaped turbo3 cache (48 layers x 8 kv heads x 32768 x 128,
     K and V as one [96, 8, 32768, 128] tensor, 6.4 GB of fp16) and a head_dim-256
-    turbo2 cache (32 layers x 4 kv heads x 32768 x 256, K and V, 4.3 GB).  Average of
-    `reps` back-to-back launches per op after ten untimed ones."""
+    turbo2 cache (32 layers x 4 kv heads x 32768 x 256, K and V, 4.3 GB); the turbo3
+    cache also through tq_pack_records / tq_unpack_records (1.26 GB each way).  Average
+    of `reps` back-to-back launches per op after ten untimed ones."""
     import torch
     out = {}
     for wname, bits in (("full_cache_14b", 3), ("head_dim_256", 2)):
@@ -434,8 +435,14 @@ def bandwidth_configs(tq, gen, dev, stream, reps=10):
         y = torch.empty_like(x)
         nblk = x.numel() // 128
         res = {"workload": f"{w.L} layers x {w.H} kv heads x {w.T} x {w.D}, K and V, turbo{bits}"}
-        for op, fn in (("encode", lambda: tq.tq_encode(bits, x, codes, norms, 0)),
-                       ("decode", lambda: tq.tq_decode(bits, codes, norms, 0, y))):
+        ops = [("encode", lambda: tq.tq_encode(bits, x, codes, norms, 0)),
+               ("decode", lambda: tq.tq_decode(bits, codes, norms, 0, y))]
+        rec = None
+        if wname == "full_cache_14b":   # the whole cache through the record layout and back
+            rec = torch.empty(nblk * (2 + 16 * bits), dtype=torch.uint8, device=dev)
+            ops += [("pack_records", lambda: tq.tq_pack_records(bits, codes, norms, rec)),
+                    ("unpack_records", lambda: tq.tq_unpack_records(bits, rec, codes, norms))]
+        for op, fn in ops:
             for _ in range(10):   # about 15 ms of load: clocks at their sustained level
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -445,12 +452,17 @@ def bandwidth_configs(tq, gen, dev, stream, reps=10):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
+            if op.endswith("records"):
+                nb = 2 * nblk * (2 + 16 * bits)
+                res[op] = {"us": round(us, 1), "bytes": nb, "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                           "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                continue
             nb = codec_bytes(nblk, bits)
             res[op] = {"us": round(us, 1), "bytes": nb, "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                        "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                        "Gvalues_per_s": round(nblk * 128 / (us * 1e-6) / 1e9, 1)}
         out[wname] = res
-        del x, y, codes, norms
+        del x, y, codes, norms, rec
         torch.cuda.empty_cache()
     return out
 
