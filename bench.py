@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the decode-step read-path timing")
+    ap.add_argument("--decode-step-only", action="store_true",
+                    help="run only the decode-step read-path timing and print its figures "
+                         "(a short run for profiling the decode attention)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the full-cache and head_dim-256 bandwidth timings")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -106,6 +109,9 @@ def main():
     torch.cuda.set_device(dev)
     tq.lib()
     stream = torch.cuda.current_stream()
+    if args.decode_step_only:
+        print(json.dumps({"decode_step": decode_step(tq, gen, dev, stream)}), flush=True)
+        return
 
     w = gen.WORKLOADS["one_layer"]
     m = D // 128
