@@ -39,6 +39,12 @@
  * passed as void* (NULL = the default stream); calls are asynchronous on it
  * and their results are valid once the caller has synchronised that stream.
  *
+ * Environment (read once per process, tuning only): TQ_ENCODE_GROUPS_PER_CU,
+ * TQ_ENCODE_ROT_GROUPS_PER_CU and TQ_DECODE_GROUPS_PER_CU cap the workgroups
+ * per compute unit of the encode / randomised-rotation encode / decode grids
+ * (0 = no cap; defaults 0, 2 and 0).  Every block is coded independently, so
+ * results are the same for every value; only the launch shape changes.
+ *
  * Errors: arguments are checked on the host before any HIP call; a failed
  * check returns a negative tq_status and launches nothing.  Work of size zero
  * returns TQ_OK and launches nothing.  A launch that HIP reports as failed
