@@ -258,6 +258,7 @@ def main():
                 "traffic": measured_traffic(dom), "bytes_per_launch": d_bytes,
                 "avg_launch_us": round(d_us, 2)}
 
+    ops_cold = cold_op_times(ops, op_values, dev, stream)   # after the timed steps: it idles the GPU
     dstep = decode_step(tq, gen, dev, stream) if not args.no_decode_step else None
     bw_cfgs = bandwidth_configs(tq, gen, dev, stream) if not args.no_large else None
     copy_ctx = copy_bandwidth(dev, stream)
@@ -288,6 +289,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": per_op,
+        "ops_cold": ops_cold,
         "rotation": rotation,
         "records": records,
         "decode_step": dstep,
@@ -473,6 +475,56 @@ def bandwidth_configs(tq, gen, dev, stream, reps=10):
     return out
 
 
+FLUSH_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
+
+
+def cold_op_times(ops, op_values, dev, stream, reps=20):
+    """Each op of the step timed alone with cold caches: before every one of `reps`
+    launches (after three untimed), a 512 MiB buffer is written so that neither the
+    op's inputs nor its predecessor's dirty lines are left in the Infinity Cache; the
+    events enclose the op only.  Median and minimum per op, GB/s and values/s at the
+    median, and encode + decode combined (sum of bytes / sum of median times)."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for name, nbytes, fn in ops:
+        times = []
+        for r in range(3 + reps):
+            scratch.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        times.sort()
+        med = times[len(times) // 2]
+        out[name] = {"median_us": round(med, 2), "min_us": round(times[0], 2), "bytes": nbytes,
+                     "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if name in op_values:
+            out[name]["Gvalues_per_s"] = round(op_values[name] / (med * 1e-6) / 1e9, 2)
+    del scratch
+    codec = [k for k in out if k.startswith(("encode_", "decode_"))]
+    nb = sum(out[k]["bytes"] for k in codec)
+    us = sum(out[k]["median_us"] for k in codec)
+    out["encode_decode_combined"] = {"ops": codec, "bytes": nb, "us": round(us, 2),
+                                     "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                                     "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
     """The CPU oracle, untuned, on whole steps of the same inputs (host copies),
     repeated until at least 10 s of CPU work."""
@@ -509,7 +561,8 @@ def cpu_baseline(KV, q, tok, scale, step_bytes, threads):
         if el >= min_seconds:
             break
     return {"value": round(step_bytes * steps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(el, 2),
+            "kind": "oracle", "seconds": round(el, 2), "cpu": cpu_model(),
+            "Gvalues_per_s_codec": round(4 * x.size * steps / el / 1e9, 4),
             "sample": f"{steps} full steps of the same workload (one layer, K and V) on host "
                       f"copies of the same inputs, repeated until at least {min_seconds:.0f} s"}
 
