@@ -258,7 +258,7 @@ def main():
                 "traffic": measured_traffic(dom), "bytes_per_launch": d_bytes,
                 "avg_launch_us": round(d_us, 2)}
 
-    ops_cold = cold_op_times(ops, op_values, dev, stream)   # after the timed steps: it idles the GPU
+    ops_cold = cold_op_times(tq, ops, op_values, dev, stream)   # after the timed steps: it idles the GPU
     dstep = decode_step(tq, gen, dev, stream) if not args.no_decode_step else None
     bw_cfgs = bandwidth_configs(tq, gen, dev, stream) if not args.no_large else None
     copy_ctx = copy_bandwidth(dev, stream)
@@ -478,23 +478,26 @@ def bandwidth_configs(tq, gen, dev, stream, reps=10):
 FLUSH_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
 
 
-def cold_op_times(ops, op_values, dev, stream, reps=20):
+def cold_op_times(tq, ops, op_values, dev, stream, reps=20):
     """Each op of the step timed alone with cold caches: before every one of `reps`
-    launches (after three untimed), a 512 MiB buffer is written so that neither the
-    op's inputs nor its predecessor's dirty lines are left in the Infinity Cache; the
-    events enclose the op only.  Median and minimum per op, GB/s and values/s at the
-    median, and encode + decode combined (sum of bytes / sum of median times)."""
+    launches (after three untimed), a 512 MiB buffer is written so that none of the
+    op's inputs is left in the Infinity Cache.  The op's kernel records its own start
+    and stop from its dispatch (tq_time_next_launch), so neither the buffer write nor
+    the host's launch latency on the idle queue is counted.  Median and minimum per
+    op, GB/s and values/s at the median, and encode + decode combined (sum of bytes /
+    sum of median times)."""
     import torch
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)   # creates the events the hook records on
+    e1.record(stream)
     out = {}
     for name, nbytes, fn in ops:
         times = []
         for r in range(3 + reps):
             scratch.fill_(float(r))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            tq.tq_time_next_launch(e0, e1)
             fn()
-            e1.record(stream)
             torch.cuda.synchronize()
             if r >= 3:
                 times.append(e0.elapsed_time(e1) * 1e3)

@@ -41,6 +41,7 @@
 // time.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -1662,20 +1663,21 @@ __global__ __launch_bounds__(256) void unpack_records_kernel(const uint8_t *__re
         norms[b0 + lane] = lr16[lane * RH];
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that race on the
+// first call store the same value).
 int cu_count()
 {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (!cache[dev]) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (!n) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // Cap on workgroups per compute unit of a codec grid, 0 for none, overridable for
