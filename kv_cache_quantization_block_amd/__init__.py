@@ -24,7 +24,9 @@ import torch
 __all__ = [
     "TQ_TURBO2", "TQ_TURBO3", "TQError", "lib", "lib_path", "header_functions",
     "tq_block_code_bytes", "tq_block_bytes", "tq_codes_nbytes", "tq_norms_count",
-    "tq_status_string", "tq_codebook", "tq_encode", "tq_decode", "tq_qk_scores", "empty_cache",
+    "tq_status_string", "tq_codebook", "tq_encode", "tq_decode", "tq_qk_scores",
+    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_pack_records", "tq_unpack_records",
+    "tq_time_next_launch", "sign_words", "empty_cache",
 ]
 
 TQ_TURBO2 = 2
@@ -157,14 +159,22 @@ def sign_words(signs):
 
 def _stream(stream) -> int | None:
     s = torch.cuda.current_stream() if stream is None else stream
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {s.device}, not the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     return s.cuda_stream or None
 
 
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    """Device pointer of t, which must be a contiguous tensor of `dtype` on the current
+    device (the library launches on the current device)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not the current device "
+                         f"cuda:{torch.cuda.current_device()} (use torch.cuda.device)")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():

@@ -31,6 +31,16 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_binding_covers_every_declared_call():
+    """Each declared call has a Python function of the same name (the _rot calls are
+    the plain functions' signs= argument), and every name the binding exports exists."""
+    for n in tq.header_functions():
+        plain = n[:-4] if n.endswith("_rot") else n
+        assert callable(getattr(tq, plain, None)), plain
+    for n in tq.__all__:
+        assert hasattr(tq, n), n
+
+
 def test_sizes():
     """Section "どこまで小さくなるのか": 128 values + one fp16 norm = 50 / 34 bytes."""
     assert tq.tq_block_code_bytes(3) == 48 and tq.tq_block_bytes(3) == 50
