@@ -339,6 +339,34 @@ def measured_traffic(kernel: str):
     return int(round((fetch + write) * 1024))
 
 
+ISSUE_FILES = {"qk": os.path.join(ROOT, "profiles", "qk_decode_step_counters.txt"),
+               "attn": os.path.join(ROOT, "profiles", "attn_partial_decode_step_counters.txt")}
+
+
+def issue_utilisation(which: str):
+    """Issue-port utilisation of the decode-step q.K ("qk") or attention partials
+    ("attn") from the committed rocprofv3 counter summary, or None when the kernel
+    source changed since it was taken.  Fractions of the kernel's cycles (GRBM_GUI_ACTIVE
+    over the 8 XCDs): VALU per SIMD and LDS per CU from SQ_ACTIVE_INST_* (4-cycle units),
+    the matrix core per SIMD from SQ_INSTS_MFMA at 16 cycles each."""
+    path = ISSUE_FILES[which]
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_code_sha256_16") != kernel_code_sha():
+        return None
+    cyc = float(rec["GRBM_GUI_ACTIVE"]) / 8
+    return {"valu_per_simd": round(float(rec["SQ_ACTIVE_INST_VALU"]) * 4 / 1024 / cyc, 3),
+            "lds_per_cu": round(float(rec["SQ_ACTIVE_INST_LDS"]) * 4 / 256 / cyc, 3),
+            "mfma_per_simd": round(float(rec["SQ_INSTS_MFMA"]) * 16 / 1024 / cyc, 3),
+            "source": os.path.relpath(path, ROOT)}
+
+
 def decode_step(tq, gen, dev, stream, reps=20):
     """Average times of the decode-step read path: per sequence turbo3 K and V caches
     of [8, 32768, 128] (16 sequences), rows 0..32766 prefilled by tq_encode; the 1-token
@@ -394,7 +422,9 @@ def decode_step(tq, gen, dev, stream, reps=20):
            "attn_us": round(med["attn"], 2), "attn_bytes": ab,
            "attn_GBps": round(ab / (med["attn"] * 1e-6) / 1e9, 1),
            "attn_frac_of_hbm_peak": round(ab / (med["attn"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "append_kv_us": round(med["append_kv"], 2)}
+           "append_kv_us": round(med["append_kv"], 2),
+           # below 70 % of HBM peak these two are bound by instruction issue
+           "qk_issue": issue_utilisation("qk"), "attn_issue": issue_utilisation("attn")}
     del kc, kn, vc, vn, scores, attn, ws
     torch.cuda.empty_cache()
     return out

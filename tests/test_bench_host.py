@@ -1,6 +1,7 @@
 """bench.py's host logic on the CPU: the kernel-code hash that keys the committed
 traffic counters ignores comments and layout but not code, the counters scale by the
-copy calibration, and more than one GPU is refused with a message."""
+copy calibration, the issue-port figures come from the committed counters, and more
+than one GPU is refused with a message."""
 import importlib.util
 import os
 import subprocess
@@ -67,3 +68,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_issue_utilisation_from_the_committed_counters(bench, monkeypatch):
+    """The decode-step q.K and attention carry their issue-port utilisation from the
+    committed counter summaries: fractions in (0, 1), and None once the kernel code no
+    longer has the hash the counters were taken with."""
+    for which in ("qk", "attn"):
+        rec = {}
+        for line in open(bench.ISSUE_FILES[which]):
+            line = line.split("#")[0].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+        monkeypatch.setattr(bench, "kernel_code_sha", lambda: rec["kernel_code_sha256_16"])
+        u = bench.issue_utilisation(which)
+        for k in ("valu_per_simd", "lds_per_cu", "mfma_per_simd"):
+            assert 0.0 < u[k] < 1.0, (which, k, u)
+        monkeypatch.setattr(bench, "kernel_code_sha", lambda: "0" * 16)
+        assert bench.issue_utilisation(which) is None
