@@ -492,7 +492,15 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
     static_assert(kEncTileBlocks * CB <= 16 * kBlock * 2, "the codes fit the output stage");
     __shared__ float lv[8];
     __shared__ uint2 ent_s[NE];
+    // randomised rotation: the sign masks of a block's 16 chunks, built once per
+    // workgroup (a wave has a single tile, so building them per lane would cost it
+    // about a sixth of its VALU work)
+    __shared__ u4_t smask_s[ROT ? 16 : 1];
     levels_to_lds(lv, cb);
+    if constexpr (ROT) {
+        if (threadIdx.x >= 64u && threadIdx.x < 80u)
+            smask_s[threadIdx.x - 64u] = sign_mask_chunk(sg, threadIdx.x - 64u);
+    }
     __syncthreads();
     // each entry is converted once (thread e), then copied: consecutive lanes write
     // consecutive copies, which meets every bank once
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
     u4_t smask[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-        smask[g] = ROT ? sign_mask_chunk(sg, 4u * g + G) : u4_t{0, 0, 0, 0};
+        smask[g] = ROT ? smask_s[4u * g + G] : u4_t{0, 0, 0, 0};
     const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)table + (lane % kLdsCopies8) * 8;
     // the wave's codes stage: block 16 c + n of the tile at (16 c + n) * 16 BITS
     uint8_t *stage = stage_all[wave];
