@@ -144,7 +144,9 @@ int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, in
  * out[b, h, :] = sum_t p_t v_hat[b, h/G, t, :] with p = softmax over rows t in [0, T)
  * of scale * q[b, h, :] . k_hat[b, h/G, t, :], G = Hq / Hkv, k_hat and v_hat the
  * decoded keys and values kept in float.  Requires D == 128, T >= 1 (when B > 0),
- * T <= Tc, Hq % Hkv == 0.  Two kernel launches on `stream`. */
+ * T <= Tc, T <= 65535 * 1024, Hq % Hkv == 0, B * Hkv * Tc <= 2^40 and
+ * B * Hq <= 2^29 - 1; larger sizes return TQ_ERR_SHAPE.  Two kernel launches on
+ * `stream`. */
 int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
                    const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
                    const void *q, int64_t Hq, float scale, float *out, void *workspace,

@@ -153,6 +153,27 @@ def test_attn_workspace_bytes():
         ws(3, 1, 8, 100, 128, 101, 32)       # T > Tc
 
 
+def test_attn_workspace_chunking_limits():
+    """The row chunking behind the workspace size: one 132-float record per (sequence,
+    query head, chunk), at most 65535 chunks (the grid's y limit) however long the
+    cache, and never more chunks than there are 256-row batches."""
+    rec = 132 * 4
+    tmax = 65535 * 1024   # longest attended range the library accepts
+    for B, Hkv, G, T in [(1, 1, 1, 1), (1, 8, 4, 32768), (16, 8, 4, 32768), (3, 2, 12, 1000),
+                         (1, 1, 1, tmax), (2, 4, 8, 33_000_000), (64, 8, 8, 131072)]:
+        Hq = Hkv * G
+        ws = tq.tq_attn_workspace_bytes(3, B, Hkv, T, 128, T, Hq)
+        assert ws > 0 and ws % (B * Hq * rec) == 0, (B, Hkv, G, T)
+        chunks = ws // (B * Hq * rec)
+        assert 1 <= chunks <= 65535, (B, Hkv, G, T, chunks)
+        assert chunks <= -(-T // 256), (B, Hkv, G, T, chunks)
+        # a longer cache never needs fewer chunks
+        if 2 * T <= tmax:
+            assert tq.tq_attn_workspace_bytes(3, B, Hkv, 2 * T, 128, 2 * T, Hq) >= ws
+    with pytest.raises(tq.TQError):
+        tq.tq_attn_workspace_bytes(3, 1, 1, tmax + 1, 128, tmax + 1, 1)
+
+
 def test_attn_validation(L):
     f = L.tq_attn_decode
     S4 = ctypes.cast(ctypes.c_void_p(S), ctypes.POINTER(ctypes.c_float))
