@@ -1699,7 +1699,7 @@ int cu_count()
 //     gain 3-7 %, one layer is unchanged).  The randomised-rotation variant keeps
 //     a persistent grid of two groups per CU: its sign masks take it to 138-142
 //     VGPRs, three waves per SIMD, where one tile per wave runs 13 % slower.
-//   decode: no cap either, one 32-block tile per wave (82-108 VGPRs and 20 / 33 KB of
+//   decode: no cap either, one 32-block tile per wave (80-106 VGPRs and 20 / 33 KB of
 //     LDS allow four to six groups per CU); caps of 5, 10 or 20 groups per CU
 //     measured slower on 8- to 48-layer caches.
 int groups_per_cu(const char *env, int dflt)
