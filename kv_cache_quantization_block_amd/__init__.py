@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(lib_path):
         raise RuntimeError(f"{lib_path} is missing; build it with "
                            "`python -m kv_cache_quantization_block_amd.build`")
+    check_build()
     L = ctypes.CDLL(lib_path)
     i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     L.tq_block_code_bytes.restype = i32
@@ -96,6 +97,21 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [i32, vp] + plain.argtypes[1:]
     _lib = L
     return L
+
+
+def check_build() -> None:
+    """Raise unless libtq.so was built from the sources now in the tree: the build
+    writes the sha256 of its sources beside the library (libtq.so.srcsha)."""
+    from . import build as _build
+    try:
+        built = open(_build.SRC_SHA).read().strip()
+    except OSError:
+        raise RuntimeError(f"{_build.SRC_SHA} is missing: rebuild libtq.so with "
+                           "`python -m kv_cache_quantization_block_amd.build`") from None
+    if built != _build.source_sha():
+        raise RuntimeError("libtq.so was built from other sources than those in "
+                           f"{_build.CSRC} and include/; rebuild it with "
+                           "`python -m kv_cache_quantization_block_amd.build`")
 
 
 def header_functions() -> list[str]:
@@ -278,7 +294,11 @@ def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_co
     T = Tc if T is None else int(T)
     need = tq_attn_workspace_bytes(type, B, Hkv, Tc, D, T, Hq)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
+        # allocated on the stream the kernels run on: the caching allocator hands these
+        # bytes to another allocation only once that stream's work is done with them
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
     if workspace.dtype != torch.uint8 or workspace.dim() != 1:
         raise ValueError("workspace must be a 1-d uint8 tensor")
     args = (_dev(k_codes, "k_codes", torch.uint8), _dev(k_norms, "k_norms", torch.float16),

@@ -18,6 +18,21 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "codebook.cpp", "api.cpp")]
+HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(ROOT, "include", "tq.h")]
+# sha256 of the sources a library was built from, written beside it at build time and
+# checked by the binding before it loads the library
+SRC_SHA = LIB + ".srcsha"
+
+
+def source_sha() -> str:
+    """sha256 over the bytes of every source and header libtq.so is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def hipcc() -> str:
@@ -36,6 +51,7 @@ def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
+    sha = source_sha()
     cmd = command(tmp)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -45,6 +61,8 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp, LIB)
+    with open(SRC_SHA, "w") as fh:
+        fh.write(sha + "\n")
     return LIB
 
 

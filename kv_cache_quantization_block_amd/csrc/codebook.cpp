@@ -102,9 +102,12 @@ void build(int bits, Codebook *cb)
         // clamping |t| at 2.6 keeps it increasing with |g| < 4 (verified below).
         cb->clamp_t = 2.6f;
     }
-    // The decision function must be increasing on [0, clamp_t], take the value k
-    // at the k-th positive threshold and stay below 2^bits/2; checked in double
-    // on the float coefficients the kernels get.
+    // The decision function must be increasing on [0, clamp_t] and stay below
+    // 2^bits/2 there, and its decision points (where it crosses k) must sit on the
+    // thresholds: checked in double on the float coefficients the kernels get.  The
+    // decision point of threshold k is found by bisection; rounding the coefficients
+    // to float moves it by less than 1e-7 (9.4e-8 at the largest turbo3 threshold),
+    // and the check allows 2e-7, about one float spacing of the thresholds.
     auto g = [cb](double t) { return t * (cb->g1 + cb->g2 * std::fabs(t) + cb->g3 * t * t); };
     double prev = 0.0;
     bool ok = true;
@@ -114,8 +117,16 @@ void build(int bits, Codebook *cb)
         prev = v;
     }
     ok = ok && g(cb->clamp_t) < P - 1e-3;
-    for (int k = 1; k < P; ++k)
-        ok = ok && std::fabs(g(th[P - 1 + k]) - k) < 1e-5;
+    for (int k = 1; k < P; ++k) {
+        const double tau = th[P - 1 + k];
+        double a = tau - 1e-3, b = tau + 1e-3;
+        ok = ok && g(a) < k && g(b) >= k;
+        for (int it = 0; it < 100; ++it) {
+            const double c = 0.5 * (a + b);
+            (g(c) < k ? a : b) = c;
+        }
+        ok = ok && std::fabs(0.5 * (a + b) - tau) < 2e-7;
+    }
     if (!ok) {
         std::fprintf(stderr, "libtq: encoder decision function check failed (bits=%d)\n", bits);
         std::abort();

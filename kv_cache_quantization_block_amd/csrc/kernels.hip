@@ -163,6 +163,37 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b)
 __device__ __forceinline__ void set_f32_round_down() { __builtin_amdgcn_s_setreg(0x801, 2); }
 __device__ __forceinline__ void set_f32_round_nearest() { __builtin_amdgcn_s_setreg(0x801, 0); }
 
+// Pins values in registers at this point of the program: an empty volatile asm that
+// takes and returns them.  Volatile asm keeps its order relative to the mode-register
+// writes, so values pinned after set_f32_round_down() are computed after it and values
+// pinned before set_f32_round_nearest() are computed before it.
+__device__ __forceinline__ void pin4(float (&v)[4])
+{
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
+// F[i] = floor(x[i] * y[i] + M) + 2^23 as a float (its low mantissa bits hold the
+// integer), for 0 <= x * y + M < 2^23: the FMA adds 2^23 + M, whose sum is a float of
+// spacing 1, under round-toward-minus-infinity.  Only these four FMAs run in that mode;
+// their operands are computed before it is set (in round-to-nearest) and their results
+// are pinned before it is cleared.
+template <int M>
+__device__ __forceinline__ void round_down_fma4(float (&x)[4], float (&y)[4], float (&F)[4])
+{
+    constexpr float magic = 8388608.0f + (float)M;   // 2^23 + M, exact
+    pin4(x);
+    pin4(y);
+    set_f32_round_down();
+    float a[4] = {x[0], x[1], x[2], x[3]}, b[4] = {y[0], y[1], y[2], y[3]};
+    pin4(a);
+    pin4(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        F[i] = __builtin_fmaf(a[i], b[i], magic);
+    pin4(F);
+    set_f32_round_nearest();
+}
+
 // The codebook levels into LDS.  Indexing the kernel-argument copy with a per-lane
 // index would turn every table entry into a round trip to memory; one lane copies
 // the levels with constant indices (scalar loads) and the caller barriers.
@@ -305,7 +336,6 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
                                                             Codebook cb, Signs sg)
 {
     constexpr int CB = 16 * BITS;         // code bytes per block
-    constexpr float mid = (float)(1 << (BITS - 1));
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWavesPerGroup][kEncTileBlocks * 48];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -396,13 +426,13 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
             const float nn = __builtin_sqrtf(a + __shfl_xor(a, 32, 64));
             nrm[c] = nn;
 
-            // 4. butterflies over g', decision, packing, staging
+            // 4. butterflies over g', decision, packing, staging.  Everything runs in
+            //    round-to-nearest except the last FMA of each decision, which adds 2^23
+            //    under round-toward-minus-infinity (see round_down_fma4).
             const float rn = nn > 0.0f ? __builtin_amdgcn_rcpf(nn) : 0.0f;
             const float k1 = cb.g1 * rn, k2 = cb.g2 * rn * rn, k3 = cb.g3 * rn * rn * rn;
             const float hi = cb.clamp_t * nn, lo = -hi;
-            constexpr float magic = 8388608.0f + mid;   // 2^23 + 2^b/2, exact
             uint32_t fb[4][8];                           // [g][position 8 G + i]: 2^23 + code
-            set_f32_round_down();
 #pragma unroll
             for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -410,21 +440,23 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
                     const float v0 = D[0][r][j], v1 = D[1][r][j], v2 = D[2][r][j], v3 = D[3][r][j];
                     const float a0 = v0 + v1, a1 = v0 - v1, a2 = v2 + v3, a3 = v2 - v3;
                     const float u[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+                    float uc[4], pp[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const float uc = __builtin_amdgcn_fmed3f(u[g], lo, hi);
-                        float F;
+                        uc[g] = __builtin_amdgcn_fmed3f(u[g], lo, hi);
                         if constexpr (BITS == 3) {
-                            float pp = __builtin_fmaf(__builtin_fabsf(uc), k3, k2);
-                            pp = __builtin_fmaf(__builtin_fabsf(uc), pp, k1);
-                            F = __builtin_fmaf(uc, pp, magic);
+                            pp[g] = __builtin_fmaf(__builtin_fabsf(uc[g]), k3, k2);
+                            pp[g] = __builtin_fmaf(__builtin_fabsf(uc[g]), pp[g], k1);
                         } else {
-                            F = __builtin_fmaf(uc, k1, magic);
+                            pp[g] = k1;
                         }
-                        fb[g][4 * r + j] = __builtin_bit_cast(uint32_t, F);
                     }
+                    float F[4];
+                    round_down_fma4<(1 << (BITS - 1))>(uc, pp, F);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        fb[g][4 * r + j] = __builtin_bit_cast(uint32_t, F[g]);
                 }
-            set_f32_round_nearest();
             uint8_t *sb = stage + (16u * c + n) * CB;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {

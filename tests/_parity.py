@@ -99,11 +99,16 @@ def check_scores(gpu, ref, qnorm, knorm, what=""):
 
 def check_attn(gpu, ref, vmax, T, what=""):
     """Decode attention [B, Hq, D]: 2e-3 of max(|r|, 1% of the head's rms), plus an
-    absolute floor T 2^-38 max|v_hat| (vmax [B, Hq], over the head's rows < T).  The
-    floor is the resolution of the weights' fp16 operands: each weight is carried to
-    2^-25 on a scale whose largest weight is 2^15, so rows far below the dominant one
-    contribute to about 2^-40 of the largest value each.  It only matters when the
-    output is many orders below the values, as when the softmax sits on a zero row."""
+    absolute floor T 2^-38 max|v_hat| (vmax [B, Hq], over the head's rows < T).
+
+    The floor bounds what the weights' finite resolution may cost.  The page's own
+    attention path dequantises K and V to fp16 and runs Flash Attention, whose P.V
+    product takes the softmax weights in fp16: with the largest weight at 1, each
+    weight is then off by up to half of fp16's smallest spacing, 2^-25, and the output
+    by up to sum_t 2^-25 |v_hat_t| / sum_t p_t <= T 2^-25 max|v_hat|.  The floor here is
+    2^13 times tighter than that bound.  It matters only where the output lies many
+    orders below the values (a softmax that sits on rows of zeros, say); elsewhere the
+    relative term dominates."""
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
@@ -114,3 +119,70 @@ def check_attn(gpu, ref, vmax, T, what=""):
     worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
     assert np.all(err <= tol), f"{what}: attention error {worst:.3f} x tolerance"
     return {"attn_worst_over_tol": worst}
+
+
+# ---------------------------------------------------------------- whole tensors
+#
+# The same rules at the workloads' full sizes, where every element is compared: the
+# oracle runs on the host, and the element-wise comparisons of large arrays run in
+# torch (float64 on the tensors' device), with the codes compared block by block and
+# unpacked only where a block differs.
+
+def check_codes_full(bits, gpu_codes, ora_codes, ora_dist, what=""):
+    """Codes of many blocks (u8 [nb, 16*bits] numpy), distances [nb, 128]: the rule of
+    check_codes, the allowance taken over all nb * 128 values."""
+    gc = np.ascontiguousarray(gpu_codes).reshape(-1, 16 * bits)
+    oc = np.ascontiguousarray(ora_codes).reshape(-1, 16 * bits)
+    d = np.asarray(ora_dist).reshape(-1, 128)
+    nvals = gc.shape[0] * 128
+    ties = int(np.count_nonzero(d < TIE_BAND))
+    bad_blk = np.nonzero((gc != oc).any(axis=1))[0]
+    nbad = 0
+    if bad_blk.size:
+        g = unpack_codes(gc[bad_blk], bits).reshape(-1)
+        o = unpack_codes(oc[bad_blk], bits).reshape(-1)
+        db = d[bad_blk].reshape(-1)
+        bad = g != o
+        nbad = int(bad.sum())
+        assert np.all(db[bad] < TIE_BAND), \
+            f"{what}: {int((db[bad] >= TIE_BAND).sum())} code mismatches outside the tie band"
+        assert np.all(np.abs(g[bad] - o[bad]) == 1), f"{what}: mismatch by more than one cell"
+    allowed = max(1, int(MISMATCH_FRAC * nvals))
+    assert nbad <= allowed, f"{what}: {nbad} tie mismatches in {nvals} values (allowed {allowed})"
+    return {"values": nvals, "mismatches": nbad, "ties": ties}
+
+
+def check_decode_torch(gpu_x16, ref, what=""):
+    """check_decode over a whole tensor: gpu_x16 a torch fp16 tensor [..., 128] (any
+    device), ref the oracle's binary64 decode (numpy, same element count)."""
+    import torch
+    g = gpu_x16.reshape(-1, 128).to(torch.float64)
+    r = torch.from_numpy(np.ascontiguousarray(ref).reshape(-1, 128)).to(g.device)
+    rms = torch.sqrt(torch.mean(r * r, dim=1, keepdim=True))
+    tol = 1e-3 * torch.maximum(r.abs(), 0.01 * rms) + 2.0 ** -25
+    over = r.abs() >= 65520.0
+    if bool(over.any()):
+        assert torch.equal(g[over], torch.sign(r[over]) * float("inf")), f"{what}: overflow not inf"
+        g = torch.where(over, r, g)
+    err = (g - r).abs()
+    worst = float((err / tol).max()) if err.numel() else 0.0
+    assert bool((err <= tol).all()), f"{what}: decode error {worst:.3f} x tolerance"
+    nz = r.abs() > 0
+    max_rel = float((err[nz] / r[nz].abs()).max()) if bool(nz.any()) else 0.0
+    return {"decode_worst_over_tol": worst, "decode_max_rel": max_rel}
+
+
+def check_scores_torch(gpu, ref, qnorm, knorm, what=""):
+    """check_scores over a whole score tensor: gpu a torch float32 tensor, ref, qnorm and
+    knorm numpy arrays broadcastable to it (float64)."""
+    import torch
+    g = gpu.to(torch.float64)
+    dev = g.device
+    r = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float64)).to(dev)
+    floor = 0.01 * torch.from_numpy(np.ascontiguousarray(qnorm, dtype=np.float64)).to(dev) * \
+        torch.from_numpy(np.ascontiguousarray(knorm, dtype=np.float64)).to(dev)
+    tol = 2e-3 * torch.maximum(r.abs(), floor)
+    err = (g - r).abs()
+    worst = float((err / tol.clamp_min(1e-300)).max()) if err.numel() else 0.0
+    assert bool((err <= tol).all()), f"{what}: score error {worst:.3f} x tolerance"
+    return {"scores": int(g.numel()), "scores_worst_over_tol": worst}

@@ -290,3 +290,27 @@ def test_timing_hook_sets_and_clears_without_a_gpu(L):
     with pytest.raises(ValueError, match="record it once"):
         tq.tq_time_next_launch(torch.cuda.Event(enable_timing=True), None)
     tq.tq_time_next_launch(None, None)
+
+
+def test_launch_failure_returns_err_device(L):
+    """A call that passes validation reaches the launch, and a launch that HIP reports
+    as failed returns TQ_ERR_DEVICE.  Forced on a host without a GPU, where every launch
+    fails (the pointers are never dereferenced); skipped wherever a GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0 or os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is visible: a launch would run")
+    E_DEVICE = -7
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    for bits in (3, 2):
+        assert L.tq_encode(bits, _p(X), 1, 2, 16, 128, _p(C), _p(N), 16, 0, None) == E_DEVICE
+        assert L.tq_decode(bits, _p(C), _p(N), 1, 2, 16, 128, 0, 16, _p(X), None) == E_DEVICE
+        assert L.tq_qk_scores(bits, _p(C), _p(N), 1, 2, 16, 128, 16, _p(Q), 8, ctypes.c_float(0.1),
+                              _p(S), None) == E_DEVICE
+        ws = L.tq_attn_workspace_bytes(bits, 1, 2, 16, 128, 16, 8)
+        assert ws > 0
+        assert L.tq_attn_decode(bits, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 16,
+                                128, 16, _p(Q), 8, ctypes.c_float(0.1), _p(S), _p(0x60000000), ws,
+                                None) == E_DEVICE
+        assert L.tq_pack_records(bits, _p(C), _p(N), 64, _p(0x60000000), None) == E_DEVICE
+        assert L.tq_unpack_records(bits, _p(0x60000000), 64, _p(C), _p(N), None) == E_DEVICE
+    assert tq.tq_status_string(E_DEVICE).startswith("TQ_ERR_DEVICE")

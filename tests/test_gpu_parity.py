@@ -255,3 +255,34 @@ def test_attn_decode_extremes(bits):
     print(_attn_case(bits, 1, 2, 4, 300, 300, seed=55, zero_rows=range(0, 300, 3)))
     print(_attn_case(bits, 1, 2, 4, 300, 300, seed=60, scale=0.3, zero_rows=range(1, 300, 2)))
     print(_attn_case(bits, 1, 2, 4, 300, 300, seed=57, scale=2.0, zero_rows=range(1, 300, 2)))
+
+
+def test_attn_decode_side_stream_without_workspace():
+    """tq_attn_decode on a side stream with no workspace given: the binding allocates the
+    workspace on that stream, so memory work queued on the default stream right after the
+    call (allocations that may reuse freed blocks, and writes into them) cannot overlap
+    the kernels' use of it; the result equals the call with a workspace of its own."""
+    bits, B, Hkv, G, Tc, T = 3, 2, 2, 4, 3000, 3000
+    k = _rand_kv(71, B, Hkv, Tc, 128)
+    v = _rand_kv(72, B, Hkv, Tc, 128)
+    kc, kn = _gpu_encode(bits, k, Tc, 0)
+    vc, vn = _gpu_encode(bits, v, Tc, 0)
+    q = gen.queries(73, B, Hkv * G, 128).cuda()
+    scale = 1.0 / math.sqrt(128)
+    ref = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_attn_workspace_bytes(bits, B, Hkv, Tc, 128, T, Hkv * G),
+                     dtype=torch.uint8, device="cuda")
+    tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, ref, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        out = torch.empty_like(ref)
+        side.wait_stream(torch.cuda.current_stream())
+        tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, out, stream=side)
+        for i in range(8):   # default-stream allocations and writes right behind the call
+            junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+            junk.fill_(float(rep * 8 + i))
+            del junk
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"repetition {rep}"

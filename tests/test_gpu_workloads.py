@@ -1,10 +1,10 @@
 """HIP path vs the CPU oracle at the evaluation workloads' full sizes (GPU).
 
 Every workload runs in the same launch configuration as bench.py (whole
-tensors, one call per op).  Where the oracle finishes in seconds (one layer)
-the comparison covers every element; at the full-cache sizes it covers whole
-layers plus random blocks, and properties that hold at any size (finite
-outputs, untouched rows, round-trip error statistics).
+tensors, one call per op), and every element is compared with the oracle: the
+whole-cache workloads one K or V layer at a time, the decode step's 16.8M
+scores and all its attention outputs at once.  Properties that hold at any size
+(finite outputs, untouched rows, round-trip error statistics) are checked too.
 """
 import math
 
@@ -15,7 +15,8 @@ import torch
 import gen
 import kv_cache_quantization_block_amd as tq
 import oracle
-from _parity import check_attn, check_codes, check_decode, check_norms, check_scores
+from _parity import (check_attn, check_codes, check_codes_full, check_decode, check_decode_torch,
+                     check_norms, check_scores_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,75 +76,116 @@ def test_one_layer_every_element(bits):
         del x, codes, norms, out
 
 
-def _sampled_full_cache(w, bits, n_random, full_layers):
-    """Encode + decode K and V of a full cache on the GPU; check whole layers and random
-    blocks against the oracle; check round-trip statistics over everything."""
-    m = w.D // 128
-    stats = {}
-    for name in ("K", "V"):
-        x = _tensor(w, name)
-        codes, norms = tq.empty_cache(bits, w.L, w.H, w.T, w.D)
-        tq.tq_encode(bits, x, codes, norms, 0)
-        out = torch.empty_like(x)
-        tq.tq_decode(bits, codes, norms, 0, out)
-        torch.cuda.synchronize()
-        assert bool(torch.isfinite(out).all()), "non-finite decoded values"
-        assert bool(torch.isfinite(norms).all()), "non-finite norms"
-        nblk = x.numel() // 128
-        rng = np.random.default_rng(w.seed * 7 + bits)
-        idx = np.unique(np.concatenate([
-            rng.integers(0, nblk, n_random),
-            np.arange(nblk - 64, nblk),
-            *[np.arange(l * w.H * w.T * m, (l + 1) * w.H * w.T * m) for l in full_layers]]))
-        it = torch.from_numpy(idx).to(DEV)
-        xb = x.view(-1, 128).index_select(0, it).cpu().numpy()
-        gc = codes.view(-1, 16 * bits).index_select(0, it).cpu().numpy()
-        gn = norms.view(-1).index_select(0, it).cpu().numpy()
-        gx = out.view(-1, 128).index_select(0, it).cpu().numpy()
-        st = _check_blocks(bits, xb, gc, gn, gx, f"{w.name} {name} turbo{bits}")
-        st["rel_mse"] = _rel_mse_per_block(x, out)
-        stats[name] = st
-        del x, codes, norms, out
-        torch.cuda.empty_cache()
-    return stats
+# ---------------------------------------------------------------- whole caches
+#
+# The whole-cache workloads run exactly as bench.py times them: K and V of every layer
+# as one [2 L, H, T, D] tensor, one encode launch over all of it, one decode launch
+# back.  The checks then stream over the cache one K or V layer at a time and compare
+# every code, norm and decoded value with the oracle.
+
+def _whole_cache(wname, bits):
+    w = gen.WORKLOADS[wname]
+    Lx = 2 * w.L
+    x = torch.empty((Lx, w.H, w.T, w.D), dtype=torch.float16, device=DEV)
+    for i, name in enumerate(("K", "V")):
+        for l in range(w.L):
+            x[i * w.L + l] = gen.kv_layer(w.seed, name, w.spec, l, w.H, w.T, w.D, device=DEV)
+    codes, norms = tq.empty_cache(bits, Lx, w.H, w.T, w.D)
+    tq.tq_encode(bits, x, codes, norms, 0)
+    y = torch.empty_like(x)
+    tq.tq_decode(bits, codes, norms, 0, y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "non-finite decoded values"
+    assert bool(torch.isfinite(norms).all()), "non-finite norms"
+    return {"w": w, "bits": bits, "x": x, "codes": codes, "norms": norms, "y": y}
 
 
-def test_full_cache_14b_turbo3():
+def _check_layers(c, layers):
+    """Every block of the given K / V layer tensors against the oracle: codes and norms
+    from the layer's fp16 input, the decode of the GPU's own codes and norms."""
+    bits, w = c["bits"], c["w"]
+    total = {"values": 0, "mismatches": 0, "ties": 0, "norm_ulp_diffs": 0,
+             "decode_worst_over_tol": 0.0, "decode_max_rel": 0.0}
+    for li in layers:
+        what = f"{w.name} {'KV'[li // w.L]} layer {li % w.L} turbo{bits}"
+        xb = c["x"][li].reshape(-1, 128).cpu().numpy()
+        gc = c["codes"][li].reshape(-1, 16 * bits).cpu().numpy()
+        gn = c["norms"][li].reshape(-1).cpu().numpy()
+        oc, on, dist = oracle.encode_blocks(bits, xb, want_dist=True)
+        st = check_codes_full(bits, gc, oc, dist, what)
+        del oc, dist
+        st.update(check_norms(gn, on, xb, what))
+        ref, _ = oracle.decode_blocks(bits, gc, gn)
+        st.update(check_decode_torch(c["y"][li], ref, what))
+        del ref
+        for k in ("values", "mismatches", "ties", "norm_ulp_diffs"):
+            total[k] += st[k]
+        for k in ("decode_worst_over_tol", "decode_max_rel"):
+            total[k] = max(total[k], st[k])
+    print(total, flush=True)
+    return total
+
+
+@pytest.fixture(scope="module")
+def full_cache_14b():
+    c = _whole_cache("full_cache_14b", 3)
+    yield c
+    c.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_full_cache_14b_turbo3_every_element(full_cache_14b, part):
     """48 layers x 8 kv heads x 32768 x 128, K and V (6.4 GB fp16): turbo3 encode of the
-    whole cache, then decode back.  Layers 0 and 47 fully plus 20000 random blocks
-    against the oracle; the mean relative round-trip error of all 25M blocks matches
-    the Gaussian turbo3 distortion (about 0.034 without outliers, lower with them)."""
-    w = gen.WORKLOADS["full_cache_14b"]
-    stats = _sampled_full_cache(w, 3, 20000, [0, w.L - 1])
-    print(stats)
-    for st in stats.values():
-        assert 0.02 < st["rel_mse"] < 0.04
+    whole cache in one launch, decode back in one; a quarter of the 96 K / V layers per
+    part, every code, norm and decoded value against the oracle."""
+    n = 2 * full_cache_14b["w"].L
+    _check_layers(full_cache_14b, range(part * n // 4, (part + 1) * n // 4))
 
 
-def test_head_dim_256_turbo2():
+def test_full_cache_14b_turbo3_distortion(full_cache_14b):
+    """The mean relative round-trip error of all 25M blocks sits at the Gaussian turbo3
+    distortion (0.0345 without outliers; the outlier channels lower it)."""
+    mse = _rel_mse_per_block(full_cache_14b["x"], full_cache_14b["y"])
+    print({"rel_mse": mse})
+    assert 0.02 < mse < 0.04
+
+
+@pytest.fixture(scope="module")
+def head_dim_256():
+    c = _whole_cache("head_dim_256", 2)
+    yield c
+    c.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_head_dim_256_turbo2_every_element(head_dim_256, part):
     """32 layers x 4 kv heads x 32768, head_dim 256 (two blocks per vector), Student-t(3)
-    outlier channels, turbo2 encode + decode.  Layer 0 fully plus 20000 random blocks
-    against the oracle; relative round-trip error near the turbo2 distortion (0.117)."""
-    w = gen.WORKLOADS["head_dim_256"]
-    stats = _sampled_full_cache(w, 2, 20000, [0])
-    print(stats)
-    for st in stats.values():
-        assert 0.05 < st["rel_mse"] < 0.13
+    outlier channels: turbo2 encode and decode of the whole cache, one launch each; a
+    quarter of the 64 K / V layers per part, every element against the oracle."""
+    n = 2 * head_dim_256["w"].L
+    _check_layers(head_dim_256, range(part * n // 4, (part + 1) * n // 4))
 
 
-def test_decode_step_read_path():
-    """Decode step: per sequence turbo3 K and V caches [8, 32768, 128] (16 sequences),
-    rows 0..32766 prefilled by tq_encode, row 32767 appended for K and V, then the
-    fused q.K of 32 query heads (GQA 4) over all 32768 rows and the fused decode
-    attention over K and V.  Appended rows, 16384 sampled scores and the attention of
-    three sampled (sequence, kv head) pairs against the oracle; the prefilled rows are
-    untouched by the append."""
+def test_head_dim_256_turbo2_distortion(head_dim_256):
+    """Relative round-trip error near the Gaussian turbo2 distortion (0.117)."""
+    mse = _rel_mse_per_block(head_dim_256["x"], head_dim_256["y"])
+    print({"rel_mse": mse})
+    assert 0.05 < mse < 0.13
+
+
+# ---------------------------------------------------------------- decode step
+
+@pytest.fixture(scope="module")
+def decode_step():
+    """Per sequence turbo3 K and V caches [8, 32768, 128] (16 sequences), rows 0..32766
+    prefilled by tq_encode, row 32767 appended for K and V (the launches bench.py times),
+    queries for 32 heads (GQA 4)."""
     w = gen.WORKLOADS["decode_step"]
     B, Hkv, T, D, Hq = w.L, w.H, w.T, w.D, w.Hq
-    G = Hq // Hkv
     bits = 3
-    caches = {}
-    toks = {}
+    c = {"w": w, "bits": bits, "B": B, "Hkv": Hkv, "T": T, "D": D, "Hq": Hq}
     for name in ("K", "V"):
         x = torch.empty((B, Hkv, T - 1, D), dtype=torch.float16, device=DEV)
         for b in range(B):
@@ -159,58 +201,82 @@ def test_decode_step_read_path():
                                   t_offset=T - 1, T_total=T)
         tq.tq_encode(bits, tok, codes, norms, T - 1)
         torch.cuda.synchronize()
-        assert torch.equal(codes[:, :, : T - 1], before_c) and torch.equal(norms[:, :, : T - 1], before_n)
+        c[name + "_untouched"] = (torch.equal(codes[:, :, : T - 1], before_c) and
+                                  torch.equal(norms[:, :, : T - 1], before_n))
         del before_c, before_n
-        caches[name] = (codes, norms)
-        toks[name] = tok
-        # the appended row against the oracle
-        tb = tok.cpu().numpy().reshape(-1, 128)
-        oc, on, dist = oracle.encode_blocks(bits, tb, want_dist=True)
-        check_codes(bits, codes[:, :, T - 1].cpu().numpy().reshape(-1, 48), oc, dist, f"append {name}")
-        check_norms(norms[:, :, T - 1].cpu().numpy(), on, tb, f"append {name}")
+        c[name] = (codes, norms)
+        c[name + "_tok"] = tok
+    c["q"] = gen.queries(w.seed, B, Hq, D, device=DEV)
+    c["scale"] = 1.0 / math.sqrt(D)
+    yield c
+    c.clear()
+    torch.cuda.empty_cache()
 
-    kc, kn = caches["K"]
-    q = gen.queries(w.seed, B, Hq, D, device=DEV)
-    scale = 1.0 / math.sqrt(D)
+
+def test_decode_step_append(decode_step):
+    """The appended row of K and V (256 blocks) against the oracle; the append leaves the
+    32767 prefilled rows of every cache untouched."""
+    c = decode_step
+    T = c["T"]
+    for name in ("K", "V"):
+        assert c[name + "_untouched"], f"append touched prefilled {name} rows"
+        codes, norms = c[name]
+        tb = c[name + "_tok"].cpu().numpy().reshape(-1, 128)
+        oc, on, dist = oracle.encode_blocks(3, tb, want_dist=True)
+        print(check_codes(3, codes[:, :, T - 1].cpu().numpy().reshape(-1, 48), oc, dist, f"append {name}"),
+              check_norms(norms[:, :, T - 1].cpu().numpy(), on, tb, f"append {name}"))
+
+
+def _decoded_norms_and_max(bits, codes, norms):
+    """Per cache row: ||k_hat|| and max |k_hat| of the oracle's decode, one sequence at a
+    time (codes [B, H, T, 1, 16 bits] numpy)."""
+    B, H, T = codes.shape[:3]
+    nrm = np.empty((B, H, T))
+    amax = np.empty((B, H, T))
+    for b in range(B):
+        xh, _ = oracle.decode_blocks(bits, codes[b].reshape(-1, 16 * bits), norms[b].reshape(-1))
+        nrm[b] = np.linalg.norm(xh, axis=1).reshape(H, T)
+        amax[b] = np.abs(xh).max(axis=1).reshape(H, T)
+        del xh
+    return nrm, amax
+
+
+def test_decode_step_qk_every_score(decode_step):
+    """q.K of 32 query heads over all 32768 rows of the 16 sequences' K caches, one
+    launch: every one of the 16.8M scores against the oracle's scores over the same
+    GPU-written cache."""
+    c = decode_step
+    B, Hkv, T, Hq = c["B"], c["Hkv"], c["T"], c["Hq"]
+    G = Hq // Hkv
+    kc, kn = c["K"]
     scores = torch.empty((B, Hq, T), dtype=torch.float32, device=DEV)
-    tq.tq_qk_scores(bits, kc, kn, q, scale, scores)
+    tq.tq_qk_scores(3, kc, kn, c["q"], c["scale"], scores)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(scores).all())
+    kcn, knn = kc.cpu().numpy(), kn.cpu().numpy()
+    qn = c["q"].cpu().numpy()
+    ref = oracle.qk_scores(3, kcn, knn, qn, c["scale"])
+    knorm, _ = _decoded_norms_and_max(3, kcn, knn)
+    qnorm = c["scale"] * np.linalg.norm(qn.astype(np.float64), axis=2)[:, :, None]
+    kn_h = np.repeat(knorm, G, axis=1)                      # query head h reads kv head h / G
+    print(check_scores_torch(scores, ref, qnorm, kn_h, "decode_step q.K"))
 
-    rng = np.random.default_rng(55)
-    ns = 16384
-    sb, sh = rng.integers(0, B, ns), rng.integers(0, Hq, ns)
-    st = rng.integers(0, T, ns)
-    st[:B * Hq] = T - 1                      # every head's appended row
-    sb[:B * Hq] = np.repeat(np.arange(B), Hq)
-    sh[:B * Hq] = np.tile(np.arange(Hq), B)
-    g = sh // G
-    blk = torch.from_numpy((sb * Hkv + g) * T + st).to(DEV)
-    gc = kc.view(-1, 48).index_select(0, blk).cpu().numpy()
-    gn = kn.view(-1).index_select(0, blk).cpu().numpy()
-    khat, _ = oracle.decode_blocks(bits, gc, gn)                       # [ns, 128]
-    qn = q.cpu().numpy().astype(np.float64)[sb, sh]                     # [ns, 128]
-    ref = scale * np.sum(qn * khat, axis=1)
-    got = scores.cpu().numpy()[sb, sh, st]
-    res = check_scores(got, ref, scale * np.linalg.norm(qn, axis=1), np.linalg.norm(khat, axis=1),
-                       "decode_step q.K")
-    print(res)
 
-    # the fused decode attention of all heads over all rows (the launch the benchmark
-    # times); three sampled (sequence, kv head) pairs, all G of their heads, against
-    # the oracle on those caches alone
-    vc, vn = caches["V"]
+def test_decode_step_attention_every_head(decode_step):
+    """The fused decode attention of 32 query heads over the 16 sequences' K and V caches
+    (all 32768 rows), one call: every output of all 128 (sequence, kv head) pairs against
+    the oracle's attention over the same GPU-written caches."""
+    c = decode_step
+    B, Hkv, T, D, Hq = c["B"], c["Hkv"], c["T"], c["D"], c["Hq"]
+    G = Hq // Hkv
+    (kc, kn), (vc, vn) = c["K"], c["V"]
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
-    tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, out)
+    tq.tq_attn_decode(3, kc, kn, vc, vn, c["q"], c["scale"], out)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
-    qh = q.cpu().numpy()
-    for b_, g_ in ((0, 0), (7, 5), (B - 1, Hkv - 1)):
-        sl = (slice(b_, b_ + 1), slice(g_, g_ + 1))
-        kcs, kns = kc[sl].cpu().numpy(), kn[sl].cpu().numpy()
-        vcs, vns = vc[sl].cpu().numpy(), vn[sl].cpu().numpy()
-        ref = oracle.attn_decode(bits, kcs, kns, vcs, vns, qh[b_:b_ + 1, g_ * G:(g_ + 1) * G], scale)
-        vhat = oracle.decode_blocks(bits, vcs.reshape(-1, 48), vns.reshape(-1))[0]
-        vmax = np.full((1, G), np.abs(vhat).max())
-        print(check_attn(out[b_:b_ + 1, g_ * G:(g_ + 1) * G].cpu().numpy(), ref, vmax, T,
-                         f"decode_step attention b={b_} g={g_}"))
+    vcn, vnn = vc.cpu().numpy(), vn.cpu().numpy()
+    ref = oracle.attn_decode(3, kc.cpu().numpy(), kn.cpu().numpy(), vcn, vnn, c["q"].cpu().numpy(),
+                             c["scale"])
+    _, vabs = _decoded_norms_and_max(3, vcn, vnn)
+    vmax = np.repeat(vabs.max(axis=2), G, axis=1)          # [B, Hq]
+    print(check_attn(out.cpu().numpy(), ref, vmax, T, "decode_step attention"))

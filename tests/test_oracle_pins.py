@@ -325,6 +325,36 @@ def test_zero_block(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 3])
+def test_norm_saturates_at_fp16_max(bits):
+    """Reading R7 (the page stores one FP16 norm per block and is silent on overflow):
+    a norm beyond the largest fp16 value is stored as 65504 (0x7BFF), not +inf, and the
+    codes are those of the unsaturated block (the normalisation uses the exact norm).
+    A norm at or beyond the rounding midpoint to infinity (65520) is the case that
+    separates saturation from plain rounding (nearest-even rounding alone would give
+    +inf there); norms below the midpoint round to nearest even as usual, and the
+    stored norm's decode scales the levels by 65504."""
+    x = np.stack([np.full(128, v, np.float16) for v in (6188.0, 5792.0, 5788.0, 5745.0)])
+    x[2, 0] = 6100.0                            # norm 65512.06: inside (65504, 65520)
+    x[:, 1::2] *= -1                            # not a Hadamard row of H alone: mixed codes
+    codes, norms, _ = oracle.encode_blocks(bits, x)
+    exact = np.linalg.norm(x.astype(np.float64), axis=1)
+    assert exact[0] > exact[1] > 65520 > exact[2] > 65504 > exact[3]
+    expect = [0x7BFF, 0x7BFF, 0x7BFF, int(np.float16(exact[3]).view(np.uint16))]
+    with np.errstate(over="ignore"):
+        assert np.float16(exact[1]) == np.inf and np.float16(exact[2]) == 65504.0
+    assert norms.view(np.uint16).tolist() == expect
+    assert not np.isinf(norms.astype(np.float64)).any()
+    # same direction, a norm far inside the range: identical codes
+    small, _, _ = oracle.encode_blocks(bits, (x.astype(np.float64) / 64).astype(np.float16))
+    assert np.array_equal(codes, small)
+    # decode of the saturated block: (65504 / 128) * H * levels, dense H (scipy)
+    lv, _, _ = oracle.codebook(bits)
+    y = lv[_unpack(codes[:1], bits)[0]]
+    xhat, _ = oracle.decode_blocks(bits, codes[:1], norms[:1])
+    assert np.allclose(xhat[0], 65504.0 / 128.0 * (H128 @ y), rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
 def test_scale_and_sign_invariance(bits):
     """encode(2x): same codes, norm doubled exactly.  encode(-x): code -> L-1-code
     wherever t is not exactly on a threshold."""
