@@ -34,8 +34,9 @@
  *
  * Memory and streams: every pointer named "device" is device memory the
  * caller owns (e.g. from torch on ROCm).  The library allocates, frees and
- * synchronises nothing and keeps no per-call state (the one exception is the
- * per-thread timing hook, tq_time_next_launch).  stream is a hipStream_t
+ * synchronises nothing and keeps no per-call state (the exceptions are the
+ * per-thread timing hook, tq_time_next_launch, and the static device scratch array
+ * that tq_attn_decode_noalloc uses instead of a workspace).  stream is a hipStream_t
  * passed as void* (NULL = the default stream); calls are asynchronous on it
  * and their results are valid once the caller has synchronised that stream.
  *
@@ -197,6 +198,27 @@ int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
                        int64_t Hkv, int64_t Tc, int64_t D, int64_t T, const void *q, int64_t Hq,
                        float scale, float *out, void *workspace, int64_t workspace_bytes,
                        void *stream);
+
+/* Decode attention that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The call of tq_attn_decode_rot (signs: as
+ * there, NULL = plain H) with the workspace taken from a static device array of
+ * TQ_ATTN_SCRATCH_BYTES inside the library: one copy per device the library runs on,
+ * held until the process ends, its address looked up once per device on the first
+ * call there.  Same arguments (less workspace and workspace_bytes), layouts, results
+ * and statuses; in addition TQ_ERR_WORKSPACE when the sizes need more than
+ * TQ_ATTN_SCRATCH_BYTES (tq_attn_workspace_bytes(...) > TQ_ATTN_SCRATCH_BYTES: about
+ * 15,000 (sequence, query head, row chunk) partials; the decode step of 16 sequences x
+ * 32 heads at 32768 rows needs 1.6 MB), and TQ_ERR_DEVICE when the array's address
+ * cannot be found.  No hipMalloc, hipFree or memset.  Every call on a device uses that
+ * device's one array: calls that overlap on the same device (other streams, other
+ * threads) race on it and must be serialised by the caller.  The array needs no initial
+ * contents (every partial is written before it is read). */
+#define TQ_ATTN_SCRATCH_BYTES (8 << 20)
+int tq_attn_decode_noalloc(int type, const uint32_t *signs, const void *k_codes,
+                           const void *k_norms, const void *v_codes, const void *v_norms,
+                           int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                           const void *q, int64_t Hq, float scale, float *out, void *stream);
 
 /* Timing hook: a measurement aid, not an operation of the codec.
  * The next kernel this thread launches through any tq_* call records its own start

@@ -25,12 +25,14 @@ __all__ = [
     "TQ_TURBO2", "TQ_TURBO3", "TQError", "lib", "lib_path", "header_functions",
     "tq_block_code_bytes", "tq_block_bytes", "tq_codes_nbytes", "tq_norms_count",
     "tq_status_string", "tq_codebook", "tq_encode", "tq_decode", "tq_qk_scores",
-    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_pack_records", "tq_unpack_records",
+    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_attn_decode_noalloc", "TQ_ATTN_SCRATCH_BYTES",
+    "tq_pack_records", "tq_unpack_records",
     "tq_time_next_launch", "sign_words", "empty_cache",
 ]
 
 TQ_TURBO2 = 2
 TQ_TURBO3 = 3
+TQ_ATTN_SCRATCH_BYTES = 8 << 20   # the static workspace of tq_attn_decode_noalloc
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtq.so")
@@ -84,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.restype = i32
     L.tq_attn_decode.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, f32, vp,
                                  vp, i64, vp]
+    L.tq_attn_decode_noalloc.restype = i32
+    L.tq_attn_decode_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64,
+                                         f32, vp, vp]
     L.tq_pack_records.restype = i32
     L.tq_pack_records.argtypes = [i32, vp, vp, i64, vp, vp]
     L.tq_unpack_records.restype = i32
@@ -310,6 +315,32 @@ def tq_attn_decode(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor, v_co
           else lib().tq_attn_decode_rot(type, sign_words(signs), *args))
     if rc:
         raise TQError(rc, "tq_attn_decode")
+
+
+def tq_attn_decode_noalloc(type: int, k_codes: torch.Tensor, k_norms: torch.Tensor,
+                           v_codes: torch.Tensor, v_norms: torch.Tensor, q: torch.Tensor,
+                           scale: float, out: torch.Tensor, T: int | None = None, stream=None,
+                           signs=None) -> None:
+    """tq_attn_decode without a workspace: the library's static device scratch array
+    (TQ_ATTN_SCRATCH_BYTES per device) takes its place, and nothing is allocated.
+    Calls that overlap on one device race on that array."""
+    B, Hkv, Tc, D = _cache_dims(k_codes, k_norms, type)
+    if _cache_dims(v_codes, v_norms, type) != (B, Hkv, Tc, D):
+        raise ValueError("K and V caches must have the same shape")
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, Hq, D] matching the cache")
+    Hq = q.shape[1]
+    if out.dim() != 3 or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    T = Tc if T is None else int(T)
+    rc = lib().tq_attn_decode_noalloc(
+        type, None if signs is None else sign_words(signs),
+        _dev(k_codes, "k_codes", torch.uint8), _dev(k_norms, "k_norms", torch.float16),
+        _dev(v_codes, "v_codes", torch.uint8), _dev(v_norms, "v_norms", torch.float16), B, Hkv,
+        Tc, D, T, _dev(q, "q", torch.float16), Hq, float(scale), _dev(out, "out", torch.float32),
+        _stream(stream))
+    if rc:
+        raise TQError(rc, "tq_attn_decode_noalloc")
 
 
 def _record_args(type: int, codes: torch.Tensor, norms: torch.Tensor, records: torch.Tensor):

@@ -347,3 +347,36 @@ int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const voi
     return tq_attn_decode_rot(type, nullptr, k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc, D, T,
                               q, Hq, scale, out, workspace, workspace_bytes, stream);
 }
+
+int tq_attn_decode_noalloc(int type, const uint32_t *signs, const void *k_codes,
+                           const void *k_norms, const void *v_codes, const void *v_norms,
+                           int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
+                           const void *q, int64_t Hq, float scale, float *out, void *stream)
+{
+    int64_t cache_blocks;
+    const int st = check_attn_shape(type, B, Hkv, Tc, D, T, Hq, &cache_blocks);
+    if (st != TQ_OK)
+        return st;
+    if (B == 0)
+        return TQ_OK;
+    if (!k_codes || !k_norms || !v_codes || !v_norms || !q || !out)
+        return TQ_ERR_NULL;
+    if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q, 16) ||
+        !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(out, 4))
+        return TQ_ERR_ALIGN;
+    if (tq::attn_workspace_bytes(type, B, Hkv, T, Hq) > TQ_ATTN_SCRATCH_BYTES)
+        return TQ_ERR_WORKSPACE;
+    const int64_t ob = B * Hq * D * 4, cb = cache_blocks * 16 * type, nb = cache_blocks * 2;
+    const void *ins[5] = {k_codes, k_norms, v_codes, v_norms, q};
+    const int64_t inb[5] = {cb, nb, cb, nb, B * Hq * D * 2};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(out, ob, ins[i], inb[i]))
+            return TQ_ERR_ALIAS;
+    void *work = tq::attn_scratch();
+    if (!work)
+        return TQ_ERR_DEVICE;
+    return tq::launch_attn(type, to_signs(signs), k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc,
+                           T, q, Hq, scale, out, work, stream)
+               ? TQ_ERR_DEVICE
+               : TQ_OK;
+}

@@ -61,6 +61,9 @@ int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_no
                 const void *v_codes, const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc,
                 int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
                 void *stream);
+// Device address of the current device's static attention scratch array (looked up
+// once per device), or nullptr when HIP cannot report it.
+void *attn_scratch();
 
 // Interleaved records (2 + 16 bits bytes per block) from / to the two planes,
 // nblocks < 2^31.

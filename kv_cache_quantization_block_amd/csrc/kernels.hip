@@ -46,6 +46,7 @@
 #include <stdlib.h>
 
 #include "internal.h"
+#include "tq.h"
 
 namespace tq {
 namespace {
@@ -1913,6 +1914,26 @@ int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
     rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
     rows = ((rows + step - 1) / step) * step;
     return rows < step ? step : rows;
+}
+
+// Workspace of tq_attn_decode_noalloc: a file-scope device array, one copy per device
+// (created when the code object is loaded there, held until the process ends).  Host
+// code never uses its name as an address: attn_scratch() looks the device address up.
+static __device__ __align__(256) uint8_t scratch[TQ_ATTN_SCRATCH_BYTES];
+
+void *attn_scratch()
+{
+    static std::atomic<void *> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {   // first call on this device, which is current: its own copy's address
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)

@@ -314,3 +314,26 @@ def test_launch_failure_returns_err_device(L):
         assert L.tq_pack_records(bits, _p(C), _p(N), 64, _p(0x60000000), None) == E_DEVICE
         assert L.tq_unpack_records(bits, _p(0x60000000), 64, _p(C), _p(N), None) == E_DEVICE
     assert tq.tq_status_string(E_DEVICE).startswith("TQ_ERR_DEVICE")
+
+
+def test_attn_noalloc_validation(L):
+    """tq_attn_decode_noalloc checks its arguments like tq_attn_decode, and refuses sizes
+    whose partials would not fit the static scratch array (TQ_ERR_WORKSPACE), all before
+    any HIP call."""
+    f = L.tq_attn_decode_noalloc
+    sc = ctypes.c_float(0.1)
+    K2, N2 = C + 0x1000000, N + 0x1000000
+    assert f(4, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_TYPE
+    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 256, 16, _p(Q), 8, sc, _p(S), None) == E_SHAPE
+    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 17, _p(Q), 8, sc, _p(S), None) == E_RANGE
+    assert f(3, None, None, _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_NULL
+    assert f(3, None, _p(C + 8), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_ALIGN
+    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(C), None) == E_ALIAS
+    assert f(3, None, None, None, None, None, 0, 2, 16, 128, 16, None, 8, sc, None, None) == OK
+    # 512 sequences x 32 heads of 256 rows: 8.65 MB of partials, beyond the 8 MiB array
+    assert L.tq_attn_workspace_bytes(3, 512, 8, 256, 128, 256, 32) > tq.TQ_ATTN_SCRATCH_BYTES
+    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 512, 8, 256, 128, 256, _p(Q), 32, sc, _p(S),
+             None) == E_WORKSPACE
+    import re
+    m = re.search(r"#define TQ_ATTN_SCRATCH_BYTES \((\d+) << (\d+)\)", open(tq.HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == tq.TQ_ATTN_SCRATCH_BYTES

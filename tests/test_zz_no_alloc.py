@@ -1,0 +1,79 @@
+"""The allocation-free decode attention, tq_attn_decode_noalloc, through the C ABI (GPU):
+its outputs equal tq_attn_decode's (same kernels, the workspace taken from the
+library's static device array instead of the caller's) on two calls in a row, the
+second one smaller, with and without the randomised rotation's signs; sizes that need
+more than TQ_ATTN_SCRATCH_BYTES are refused before any launch."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import kv_cache_quantization_block_amd as tq
+
+pytestmark = pytest.mark.gpu
+
+SPEC = gen.KVSpec(n_outliers=3, row_scale=True)
+
+
+def _cache(bits, seed, name, B, Hkv, T):
+    x = torch.empty((B, Hkv, T, 128), dtype=torch.float16, device="cuda")
+    for b in range(B):
+        x[b] = gen.kv_layer(seed, name, SPEC, b, Hkv, T, 128, device="cuda")
+    codes, norms = tq.empty_cache(bits, B, Hkv, T, 128, "cuda")
+    tq.tq_encode(bits, x, codes, norms, 0)
+    return codes, norms
+
+
+def _noalloc_c_abi(bits, signs, kc, kn, vc, vn, q, scale, out, T):
+    """Direct ctypes call of the C entry point (NULL stream: the default stream)."""
+    B, Hkv, Tc = kc.shape[:3]
+    Hq = q.shape[1]
+    w = None if signs is None else tq.sign_words(signs)
+    return tq.lib().tq_attn_decode_noalloc(bits, w, kc.data_ptr(), kn.data_ptr(), vc.data_ptr(),
+                                           vn.data_ptr(), B, Hkv, Tc, 128, T, q.data_ptr(), Hq,
+                                           ctypes.c_float(scale), out.data_ptr(), None)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_noalloc_attention_equals_workspace_attention(bits):
+    torch.cuda.set_device(0)
+    scale = 1.0 / math.sqrt(128)
+    signs = np.where(np.random.default_rng(9).random(128) < 0.5, -1.0, 1.0)
+    # two calls in a row, the second one smaller (fewer sequences, heads and rows)
+    for i, (B, Hkv, G, Tc, T) in enumerate(((4, 8, 4, 8192, 8192), (2, 2, 4, 1200, 1000))):
+        kc, kn = _cache(bits, 30 + i, "K", B, Hkv, Tc)
+        vc, vn = _cache(bits, 30 + i, "V", B, Hkv, Tc)
+        q = gen.queries(40 + i, B, Hkv * G, 128, device="cuda")
+        need = tq.tq_attn_workspace_bytes(bits, B, Hkv, Tc, 128, T, Hkv * G)
+        assert 0 < need <= tq.TQ_ATTN_SCRATCH_BYTES
+        for sg in (None, signs):
+            ref = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, ref, T=T, workspace=ws, signs=sg)
+            out = torch.full_like(ref, float("nan"))
+            torch.cuda.synchronize()
+            assert _noalloc_c_abi(bits, sg, kc, kn, vc, vn, q, scale, out, T) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), (i, sg is None)
+            # the binding of the same call
+            out2 = torch.full_like(ref, float("nan"))
+            tq.tq_attn_decode_noalloc(bits, kc, kn, vc, vn, q, scale, out2, T=T, signs=sg)
+            torch.cuda.synchronize()
+            assert torch.equal(out2, ref), (i, sg is None)
+
+
+def test_noalloc_attention_refuses_sizes_beyond_the_scratch():
+    """Sizes whose partials need more than TQ_ATTN_SCRATCH_BYTES: TQ_ERR_WORKSPACE, before
+    any launch (the pointers are valid device memory, never read)."""
+    bits, B, Hkv, G, T = 3, 512, 8, 4, 256
+    need = tq.tq_attn_workspace_bytes(bits, B, Hkv, T, 128, T, Hkv * G)
+    assert need > tq.TQ_ATTN_SCRATCH_BYTES
+    kc, kn = tq.empty_cache(bits, B, Hkv, T, 128, "cuda")
+    q = torch.zeros((B, Hkv * G, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    assert _noalloc_c_abi(bits, None, kc, kn, kc, kn, q, 0.1, out, T) == -8
+    with pytest.raises(tq.TQError, match="WORKSPACE"):
+        tq.tq_attn_decode_noalloc(bits, kc, kn, kc, kn, q, 0.1, out, T=T)
