@@ -107,6 +107,11 @@ __device__ __forceinline__ T lds_load(uint32_t addr)
 // each reading its own copy, never collide whatever entries they pick.
 constexpr int kLdsCopies8 = 32;
 
+// Threads of every workgroup these kernels launch with.  Loops step by this constant,
+// not by blockDim.x: reading blockDim.x is a load from the dispatch packet, and the
+// wait for it would also wait for every load issued before it (loads complete in order).
+constexpr uint32_t kGroupThreads = kWavesPerGroup * kWave;
+
 
 // The value of another lane of the same quad (DPP quad_perm pattern CTRL).
 template <int CTRL>
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
         ent_s[e] = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
     }
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += blockDim.x)
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(NE * kLdsCopies8); i += kGroupThreads)
         *(uint2 *)(table + i * 8) = ent_s[i / kLdsCopies8];
     __syncthreads();
 
@@ -777,7 +782,7 @@ __device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv, u
 {
     using Tb = QkTable<BITS>;
     static_assert(Tb::NE * Tb::EB <= 16 * kBlock * 2, "the entries fit one block's query operands");
-    for (uint32_t e = threadIdx.x; e < (uint32_t)Tb::NE; e += blockDim.x) {
+    for (uint32_t e = threadIdx.x; e < (uint32_t)Tb::NE; e += kGroupThreads) {
         if constexpr (BITS == 3) {
             _Float16 a0, a1, c0, c1;
             split_f16(lv[e & 7], a0, c0);
@@ -793,7 +798,7 @@ __device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv, u
         }
     }
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(Tb::NE * Tb::NC); i += blockDim.x) {
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(Tb::NE * Tb::NC); i += kGroupThreads) {
         if constexpr (BITS == 3)
             *(uint2 *)(table + i * Tb::EB) = *(const uint2 *)(scratch + (i / Tb::NC) * Tb::EB);
         else
@@ -809,18 +814,37 @@ __device__ __forceinline__ void qk_fill_table(uint8_t *table, const float *lv, u
 // 2^(14 - e) as hi (row hh) and lo (row 8 + hh) of qa [m][16][128], and 2^(e - 14) to
 // pw_s[hh].  Heads past nh get zero rows.  The caller barriers afterwards.  With the
 // randomised rotation q' = H D q, since q . (D H y) = (H D q) . y.
+// The query values lane `lane` of wave `wave` rotates when D == 128 (positions lane and
+// 64 + lane of its two heads' rows), loaded at the very start of a kernel: issued before
+// the first key codes, they do not wait behind them (loads complete in order).  Heads
+// past nh read head h0's row instead (never used).
+__device__ __forceinline__ void qk_load_queries(uint16_t (&pre)[2][2], const uint16_t *__restrict__ q,
+                                                uint32_t b, uint32_t Hq, uint32_t h0, uint32_t nh,
+                                                uint32_t wave, uint32_t lane)
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t hh = wave + kWavesPerGroup * s;
+        const uint16_t *qv = q + ((size_t)b * Hq + h0 + (hh < nh ? hh : 0u)) * kBlock;
+        pre[s][0] = ld_stream(qv + lane);
+        pre[s][1] = ld_stream(qv + 64 + lane);
+    }
+}
+
 template <bool ONE_BLOCK>
 __device__ __forceinline__ void qk_prepare_queries(_Float16 *qa, float *pw_s,
                                                    const uint16_t *__restrict__ q, uint32_t b,
                                                    uint32_t Hq, uint32_t h0, uint32_t nh,
                                                    uint32_t m, uint32_t wave, uint32_t lane,
-                                                   float scale, const Signs &sg)
+                                                   float scale, const Signs &sg,
+                                                   const uint16_t (&pre)[2][2])
 {
     const uint16_t fa = (uint16_t)(sign_mask_f32(sg, lane) >> 16);
     const uint16_t fc = (uint16_t)(sign_mask_f32(sg, 64u + lane) >> 16);
-    auto rotate = [&](const uint16_t *v, float &a, float &c) {
-        a = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[lane] ^ fa));
-        c = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[64 + lane] ^ fc));
+    // the slice's two values (from memory, or preloaded by qk_load_queries: D == 128)
+    auto rotate_v = [&](uint16_t va, uint16_t vc, float &a, float &c) {
+        a = (float)__builtin_bit_cast(_Float16, (uint16_t)(va ^ fa));
+        c = (float)__builtin_bit_cast(_Float16, (uint16_t)(vc ^ fc));
         const float s0 = a + c;
         c = a - c;
         a = s0;
@@ -832,14 +856,21 @@ __device__ __forceinline__ void qk_prepare_queries(_Float16 *qa, float *pw_s,
             c = up ? pc - c : c + pc;
         }
     };
-    for (uint32_t hh = wave; hh < (uint32_t)kQkHeads; hh += kWavesPerGroup) {
+    auto rotate = [&](const uint16_t *v, float &a, float &c) { rotate_v(v[lane], v[64 + lane], a, c); };
+    static_assert(kQkHeads == 2 * kWavesPerGroup, "two preloaded head slots per wave");
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+        const uint32_t hh = wave + kWavesPerGroup * slot;
         _Float16 *hi_row = qa + hh * kBlock, *lo_row = qa + (kQkHeads + hh) * kBlock;
         if (hh < nh) {
             const uint16_t *qv = q + ((size_t)b * Hq + h0 + hh) * ((size_t)m * kBlock);
             float mx = 0.0f, a1 = 0.0f, c1 = 0.0f;   // a1, c1: the single slice when m == 1
             for (uint32_t j = 0; j < m; ++j) {
                 float a, c;
-                rotate(qv + j * kBlock, a, c);
+                if (ONE_BLOCK)
+                    rotate_v(pre[slot][0], pre[slot][1], a, c);
+                else
+                    rotate(qv + j * kBlock, a, c);
                 mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(c)));
                 a1 = a;
                 c1 = c;
@@ -985,6 +1016,9 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
         na = ld_stream(k_norms + row0 + ta);
         nb = ld_stream(k_norms + row0 + tb);
     };
+    uint16_t qpre[2][2] = {{0, 0}, {0, 0}};
+    if constexpr (ONE_BLOCK)   // the queries first: their wait does not cover the codes
+        qk_load_queries(qpre, q, b, Hq, h0, nh, wave, lane);
     uint32_t wn[kQkDepth][LW];
     uint16_t nn[kQkDepth];
     // (16-bit, widened only where used: a widening right after the load would wait
@@ -1001,7 +1035,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     __syncthreads();
     qk_fill_table<BITS>(table, lv, (uint8_t *)qa);   // qa is written only below
 
-    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg);
+    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg, qpre);
     __syncthreads();
 
     // A operands of block j for this lane's row (lane % 16) and value run
@@ -1304,9 +1338,11 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     };
     // a batch's codes and norms; each unit's registers are refilled with the next
     // batch's unit as soon as they have been consumed
+    uint16_t qpre[2][2];
+    qk_load_queries(qpre, q, b, Hq, h0, nh, wave, lane);   // first: see qk_load_queries
     uint32_t wk[kAttnDepth][LW], wv[kAttnDepth][LW];
     uint32_t nkc = 0, nvc = 0;
-    fetch_norms(0, nkc, nvc);   // norms first, as in the loop
+    fetch_norms(0, nkc, nvc);   // norms next, as in the loop
 #pragma unroll
     for (int d = 0; d < kAttnDepth; ++d)
         fetch(d, wk[d], wv[d]);
@@ -1316,7 +1352,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     __syncthreads();
     qk_fill_table<BITS>(ktable, lv, (uint8_t *)qa);   // qa is written only below
     if constexpr (BITS == 2) {
-        for (uint32_t i = threadIdx.x; i < 16u * kLdsCopies8; i += blockDim.x) {
+        for (uint32_t i = threadIdx.x; i < 16u * kLdsCopies8; i += kGroupThreads) {
             const uint32_t e = i / kLdsCopies8;
             _Float16 a0, c0, a1, c1;
             split_f16(lv[e & 3u], a0, c0);
@@ -1324,7 +1360,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
             *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         }
     }
-    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale, sg);
+    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale, sg, qpre);
     __syncthreads();
 
     h8_t A[8];
