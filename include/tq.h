@@ -144,9 +144,11 @@ int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, in
  *              contents needed; calls that share a workspace must not overlap
  * out[b, h, :] = sum_t p_t v_hat[b, h/G, t, :] with p = softmax over rows t in [0, T)
  * of scale * q[b, h, :] . k_hat[b, h/G, t, :], G = Hq / Hkv, k_hat and v_hat the
- * decoded keys and values kept in float.  Requires D == 128, T >= 1 (when B > 0),
- * T <= Tc, T <= 65535 * 1024, Hq % Hkv == 0, B * Hkv * Tc <= 2^40 and
- * B * Hq <= 2^29 - 1; larger sizes return TQ_ERR_SHAPE.  Two kernel launches on
+ * decoded keys and values kept in float.  D is 128 or 256 (section "実モデルでの数値":
+ * a head_dim of 256 is two stacked blocks, each with its own norm; a row's score sums
+ * both blocks' dot products).  Requires T >= 1 (when B > 0), T <= Tc,
+ * T <= 65535 * 1024, Hq % Hkv == 0, B * Hkv * Tc * D / 128 <= 2^40 and
+ * B * Hq <= 2^29 - 1; other sizes return TQ_ERR_SHAPE.  Two kernel launches on
  * `stream`. */
 int tq_attn_decode(int type, const void *k_codes, const void *k_norms, const void *v_codes,
                    const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,

@@ -274,19 +274,19 @@ int tq_time_next_launch(void *start_event, void *stop_event)
 
 }  // extern "C"
 
-// Shapes of the decode attention call (D = 128); fills the cache blocks of one cache.
+// Shapes of the decode attention call (D = 128 or 256); fills the cache blocks of one cache.
 static int check_attn_shape(int type, int64_t B, int64_t Hkv, int64_t Tc, int64_t D, int64_t T,
                             int64_t Hq, int64_t *cache_blocks)
 {
     if (!valid_type(type))
         return TQ_ERR_TYPE;
-    if (B < 0 || Hkv <= 0 || Hq <= 0 || Tc < 0 || T < 0 || D != tq::kBlock || Hq % Hkv ||
-        (B > 0 && T < 1))
+    if (B < 0 || Hkv <= 0 || Hq <= 0 || Tc < 0 || T < 0 ||
+        (D != tq::kBlock && D != 2 * tq::kBlock) || Hq % Hkv || (B > 0 && T < 1))
         return TQ_ERR_SHAPE;
     if (T > Tc)
         return TQ_ERR_RANGE;
     int64_t nq;
-    if (!mul4(B, Hkv, Tc, 1, cache_blocks) || *cache_blocks > ((int64_t)1 << 40) ||
+    if (!mul4(B, Hkv, Tc, D / tq::kBlock, cache_blocks) || *cache_blocks > ((int64_t)1 << 40) ||
         !mul4(B, Hq, D, 1, &nq) || T > 65535LL * 1024 || B * Hq > INT32_MAX / 4)
         return TQ_ERR_SHAPE;
     return TQ_OK;
@@ -301,7 +301,7 @@ int64_t tq_attn_workspace_bytes(int type, int64_t B, int64_t Hkv, int64_t Tc, in
         return st;
     if (B == 0)
         return 0;
-    return tq::attn_workspace_bytes(type, B, Hkv, T, Hq);
+    return tq::attn_workspace_bytes(type, B, Hkv, T, Hq, D / tq::kBlock);
 }
 
 int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
@@ -322,7 +322,7 @@ int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
         !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(out, 4) ||
         !aligned(workspace, 16))
         return TQ_ERR_ALIGN;
-    const int64_t need = tq::attn_workspace_bytes(type, B, Hkv, T, Hq);
+    const int64_t need = tq::attn_workspace_bytes(type, B, Hkv, T, Hq, D / tq::kBlock);
     if (workspace_bytes < need)
         return TQ_ERR_WORKSPACE;
     const int64_t ob = B * Hq * D * 4, cb = cache_blocks * 16 * type, nb = cache_blocks * 2;
@@ -334,7 +334,7 @@ int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
     if (overlap(out, ob, workspace, need))
         return TQ_ERR_ALIAS;
     return tq::launch_attn(type, to_signs(signs), k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc,
-                           T, q, Hq, scale, out, workspace, stream)
+                           D / tq::kBlock, T, q, Hq, scale, out, workspace, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
 }
@@ -364,7 +364,7 @@ int tq_attn_decode_noalloc(int type, const uint32_t *signs, const void *k_codes,
     if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q, 16) ||
         !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(out, 4))
         return TQ_ERR_ALIGN;
-    if (tq::attn_workspace_bytes(type, B, Hkv, T, Hq) > TQ_ATTN_SCRATCH_BYTES)
+    if (tq::attn_workspace_bytes(type, B, Hkv, T, Hq, D / tq::kBlock) > TQ_ATTN_SCRATCH_BYTES)
         return TQ_ERR_WORKSPACE;
     const int64_t ob = B * Hq * D * 4, cb = cache_blocks * 16 * type, nb = cache_blocks * 2;
     const void *ins[5] = {k_codes, k_norms, v_codes, v_norms, q};
@@ -376,7 +376,7 @@ int tq_attn_decode_noalloc(int type, const uint32_t *signs, const void *k_codes,
     if (!work)
         return TQ_ERR_DEVICE;
     return tq::launch_attn(type, to_signs(signs), k_codes, k_norms, v_codes, v_norms, B, Hkv, Tc,
-                           T, q, Hq, scale, out, work, stream)
+                           D / tq::kBlock, T, q, Hq, scale, out, work, stream)
                ? TQ_ERR_DEVICE
                : TQ_OK;
 }

@@ -53,14 +53,14 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
               int64_t Hkv, int64_t Tc, int64_t m, int64_t T, const void *q, int64_t Hq,
               float scale, float *scores, void *stream);
 
-// Decode attention (D = 128): rows per chunk and workspace bytes follow from the sizes
-// alone; the launch runs the partial and the combine kernel.
-int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
-int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq);
+// Decode attention (D = 128 m, m = 1 or 2): rows per chunk and workspace bytes follow
+// from the sizes alone; the launch runs the partial and the combine kernel.
+int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq, int64_t m);
+int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq, int64_t m);
 int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_norms,
                 const void *v_codes, const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc,
-                int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
-                void *stream);
+                int64_t m, int64_t T, const void *q, int64_t Hq, float scale, float *out,
+                void *work, void *stream);
 // Device address of the current device's static attention scratch array (looked up
 // once per device), or nullptr when HIP cannot report it.
 void *attn_scratch();

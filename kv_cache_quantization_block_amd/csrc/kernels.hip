@@ -1244,12 +1244,14 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 // larger E rescales acc by a power of two, the way a larger score rescales it by
 // exp(m_old - m_new).
 
-constexpr int kAttnDepth = 4;          // 16-row units in flight per wave
-// Workgroups per CU: LDS (41 KB turbo3, 62 KB turbo2) and VGPRs allow three turbo3
-// groups, two turbo2; also the target of the row chunking.
+// Workgroups per CU: LDS (41 / 45 KB turbo3, 62 / 66 KB turbo2 for head_dim 128 / 256)
+// and VGPRs allow three turbo3 groups, two turbo2; also the target of the row chunking.
 constexpr int attn_groups_per_cu(int bits) { return bits == 3 ? 3 : 2; }
-constexpr int kAttnRaw = 16 * 48;      // bytes of a wave's packed-code tile (16 rows)
-constexpr int kAttnRec = 4 + kBlock;   // workspace floats per partial: m, l, -, -, acc[128]
+// M = blocks per row (head_dim 128 M).  A batch is 64 / M rows (4 / M 16-row units), so
+// that one norm load per lane covers its 64 (row, block) norms and the units in flight
+// hold the same bytes for both head dims.
+constexpr int attn_depth(int M) { return 4 / M; }
+constexpr int attn_rec(int M) { return 4 + kBlock * M; }   // workspace floats per partial: m, l, -, -, acc
 constexpr int kAttnWExp = 15;          // the weights' power-of-two headroom below fp16's max
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -1262,7 +1264,9 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 constexpr int attn_vtable_bytes(int bits) { return bits == 3 ? 0 : 16 * kLdsCopies8 * 8; }
 
 // NHS: sets of four query heads per pass (1: up to four heads, 2: up to eight).
-template <int BITS, int NHS>
+// M: 128-blocks per row (1 or 2); each row's score sums its blocks' dot products, each
+// block has its own value norms, weights and P.V accumulators.
+template <int BITS, int NHS, int M>
 __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_kernel(
     const uint8_t *__restrict__ k_codes, const uint16_t *__restrict__ k_norms,
     const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
@@ -1271,19 +1275,23 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     float scale, Codebook cb, Signs sg)
 {
     constexpr int NC = QkTable<BITS>::NC, EB = QkTable<BITS>::EB;
-    constexpr int CB = 16 * BITS;   // code bytes per block
-    constexpr int LW = BITS;        // code words per lane (32 codes)
-    // LDS: the tables; per unit in flight the packed value codes of its 16 rows (48-byte
-    // rows, one spare dword read past the last field) and the weights [head][row] as
+    constexpr int CB = 16 * BITS;        // code bytes per block
+    constexpr int LW = BITS;             // code words per lane and block (32 codes)
+    constexpr int DEPTH = attn_depth(M); // units per batch
+    constexpr int REC = attn_rec(M);
+    constexpr int RW = 12 * M;           // words per token row of a code tile (48 B per block)
+    // LDS: the tables; per unit in flight the packed value codes of its 16 rows (one
+    // spare dword read past the last field) and, per block, the weights [head][row] as
     // (hi, lo); after the last unit the same bytes hold the four waves' states
     constexpr int kTables = qk_table_bytes(BITS) + attn_vtable_bytes(BITS);
-    constexpr int kRawWords = kAttnRaw / 4 + 4;
-    constexpr int kRawBytes = kAttnDepth * kWavesPerGroup * kRawWords * 4;
-    constexpr int kPtBytes = kAttnDepth * kWavesPerGroup * kQkHeads * 16 * 4;
-    constexpr int kMerge = kWavesPerGroup * kQkHeads * kAttnRec * 4;
+    constexpr int kRawWords = 16 * RW + 4;
+    constexpr int kRawBytes = DEPTH * kWavesPerGroup * kRawWords * 4;
+    constexpr int kPtBytes = DEPTH * M * kWavesPerGroup * kQkHeads * 16 * 4;
+    constexpr int kMerge = kWavesPerGroup * kQkHeads * REC * 4;
     static_assert(kMerge <= kTables + kRawBytes + kPtBytes, "the merge reuses the tiles' bytes");
+    static_assert(DEPTH * 16 * M == 64, "one norm load per lane per batch");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kTables + kRawBytes + kPtBytes];
-    __shared__ __attribute__((aligned(16))) _Float16 qa[16 * kBlock];
+    __shared__ __attribute__((aligned(16))) _Float16 qa[M * 16 * kBlock];
     __shared__ __attribute__((aligned(16))) float ftile[kWavesPerGroup][kQkHeads];
     __shared__ float pw_s[kQkHeads];
     __shared__ float lv[8];
@@ -1310,41 +1318,44 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     const uint32_t last = min(t_end, first + wspan);
     const uint32_t nunits = first < last ? (last - first + 15u) / 16u : 0u;
 
-    // K and V codes of this lane's run (row n, values 32 part ..) of unit k, and a
-    // batch's norms (row first + 16 k + lane, one per lane: kAttnDepth units = 64 rows).
-    // Rows past the wave's range are clamped to its last row (a wave without rows: the
-    // chunk's last), so the loads are unconditional, stay in bounds and re-read lines
-    // the wave has just fetched; their values are never used.
+    // K and V codes of this lane's run (row n, values 32 part ..) of every block of unit
+    // k, and a batch's norms (element (row, block) of the batch's 64 / M rows, one per
+    // lane).  Rows past the wave's range are clamped to its last row (a wave without
+    // rows: the chunk's last), so the loads are unconditional, stay in bounds and
+    // re-read lines the wave has just fetched; their values are never used.
     const uint32_t lastc = nunits ? last - 1u : t_end - 1u;
-    auto fetch = [&](uint32_t k, uint32_t (&wk)[LW], uint32_t (&wv)[LW]) {
+    auto fetch = [&](uint32_t k, uint32_t (&wk)[M][LW], uint32_t (&wv)[M][LW]) {
         const uint32_t tb = min(first + k * 16u, lastc);                 // wave-uniform
         const uint32_t r = min(n, lastc - tb);
-        const uint32_t lo = __umul24(r, (uint32_t)CB) + part * (4 * BITS);
-        const size_t ub = (row0 + tb) * CB;                              // wave-uniform
-        const uint32_t *kp = (const uint32_t *)(k_codes + ub + lo);
-        const uint32_t *vp = (const uint32_t *)(v_codes + ub + lo);
+        const size_t ub = (row0 + tb) * (M * CB);                        // wave-uniform
 #pragma unroll
-        for (int i = 0; i < LW; ++i) {
-            wk[i] = ld_stream(kp + i);
-            wv[i] = ld_stream(vp + i);
+        for (int jb = 0; jb < M; ++jb) {
+            const uint32_t lo = __umul24(r, (uint32_t)(M * CB)) + jb * CB + part * (4 * BITS);
+            const uint32_t *kp = (const uint32_t *)(k_codes + ub + lo);
+            const uint32_t *vp = (const uint32_t *)(v_codes + ub + lo);
+#pragma unroll
+            for (int i = 0; i < LW; ++i) {
+                wk[jb][i] = ld_stream(kp + i);
+                wv[jb][i] = ld_stream(vp + i);
+            }
         }
     };
-    static_assert(kAttnDepth * 16 == 64, "one norm load per lane per batch");
     auto fetch_norms = [&](uint32_t k, uint32_t &nk, uint32_t &nv) {
         const uint32_t tb = min(first + 16u * k, lastc);                 // wave-uniform
-        const uint32_t r = min(lane, lastc - tb);
-        nk = ld_stream(k_norms + (row0 + tb) + r);
-        nv = ld_stream(v_norms + (row0 + tb) + r);
+        const uint32_t e = min(lane, (lastc - tb) * M + (M - 1));
+        nk = ld_stream(k_norms + (row0 + tb) * M + e);
+        nv = ld_stream(v_norms + (row0 + tb) * M + e);
     };
     // a batch's codes and norms; each unit's registers are refilled with the next
     // batch's unit as soon as they have been consumed
-    uint16_t qpre[2][2];
-    qk_load_queries(qpre, q, b, Hq, h0, nh, wave, lane);   // first: see qk_load_queries
-    uint32_t wk[kAttnDepth][LW], wv[kAttnDepth][LW];
+    uint16_t qpre[2][2] = {{0, 0}, {0, 0}};
+    if constexpr (M == 1)   // the queries first: see qk_load_queries
+        qk_load_queries(qpre, q, b, Hq, h0, nh, wave, lane);
+    uint32_t wk[DEPTH][M][LW], wv[DEPTH][M][LW];
     uint32_t nkc = 0, nvc = 0;
     fetch_norms(0, nkc, nvc);   // norms next, as in the loop
 #pragma unroll
-    for (int d = 0; d < kAttnDepth; ++d)
+    for (int d = 0; d < DEPTH; ++d)
         fetch(d, wk[d], wv[d]);
 
     // tables and query operands
@@ -1360,19 +1371,23 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
             *(uint2 *)(vtable + i * 8) = uint2{pack_h2(a0, a1), pack_h2(c0, c1)};
         }
     }
-    qk_prepare_queries<true>(qa, pw_s, q, b, Hq, h0, nh, 1u, wave, lane, scale, sg, qpre);
+    qk_prepare_queries<M == 1>(qa, pw_s, q, b, Hq, h0, nh, (uint32_t)M, wave, lane, scale, sg, qpre);
     __syncthreads();
 
-    h8_t A[8];
-    {
-        const _Float16 *arow = qa + n * kBlock + part * 32;
+    // query operands of block jb for this lane's row (lane % 16) and value run; one
+    // block: kept in registers, two: read from LDS where they are used
+    auto load_a = [&](uint32_t jb, h8_t (&Aj)[8]) {
+        const _Float16 *arow = qa + jb * 2048 + n * kBlock + part * 32;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const uint32_t *p = (const uint32_t *)(arow + 4 * c);
             const uint32_t x01 = p[0], x23 = p[1];
-            A[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
+            Aj[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
         }
-    }
+    };
+    h8_t A[8];
+    if constexpr (M == 1)
+        load_a(0, A);
     const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)ktable + (lane % NC) * EB;
     const uint32_t vcopy = (uint32_t)(uintptr_t)(lds_u8 *)vtable + (lane % kLdsCopies8) * 8;
     // after the hi/lo combine, lane l holds heads hu and hu + 2 of token l % 16
@@ -1380,8 +1395,8 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     // scores in log2 units, so that every exponential is a bare 2^x
     const float pw_u = pw_s[hu] * kLog2e, pw_v = pw_s[hu + 2] * kLog2e;
     float *ft = ftile[wave];
-    // this lane's 8-value field in a token row of the code tile (column n: values
-    // 8 n .. 8 n + 7): dwords dA, dA + 1 of the row, shifted by fsh
+    // this lane's 8-value field in a block of a token row of the code tile (column n:
+    // values 8 n .. 8 n + 7): dwords dA, dA + 1 of the block's 12, shifted by fsh
     constexpr int FBITS = 8 * BITS;
     const uint32_t dA = (FBITS * n) >> 5, fsh = (FBITS * n) & 31u;
     // A rows: lane n of a lane group is row n = 8 hilo + 2 hh + e.  A token's four
@@ -1397,51 +1412,66 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
 
     // online softmax state: running max and sum of heads hu, hu + 2 (the same in all 16
     // lanes of a row), the value-norm exponent E (wave-wide) and the P.V accumulators
-    // (head set s, product block c: rows 4 (lane / 16) .. + 3, column lane % 16)
+    // (block jb, head set hs, product block c: rows 4 (lane / 16) .. + 3, column lane % 16)
     float m_u = -__builtin_inff(), m_v = -__builtin_inff(), l_u = 0.0f, l_v = 0.0f;
     int E = -1000;
-    f4_t acc[NHS][4];
+    f4_t acc[M][NHS][4];
 #pragma unroll
-    for (int hs = 0; hs < NHS; ++hs)
+    for (int jb = 0; jb < M; ++jb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            acc[hs][c] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int hs = 0; hs < NHS; ++hs)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[jb][hs][c] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-
-    // batches of units k0 .. k0 + kAttnDepth - 1 (unit k0 holds a live row); the next
+    // batches of units k0 .. k0 + DEPTH - 1 (unit k0 holds a live row); the next
     // batch's norms are requested first, so that they are the oldest loads in flight
     // when that batch starts
-    for (uint32_t k0 = 0; k0 < nunits; k0 += kAttnDepth) {
+    for (uint32_t k0 = 0; k0 < nunits; k0 += DEPTH) {
         uint32_t nkn, nvn;
-        fetch_norms(k0 + kAttnDepth, nkn, nvn);
-        // scores of heads hu, hu + 2 for token n of each unit (as qk_kernel), -inf past
-        // the range; the units' packed value codes into their tiles (row n, bytes
-        // 4 BITS part ..)
-        float su[kAttnDepth], sv[kAttnDepth], nvd[kAttnDepth];
+        fetch_norms(k0 + DEPTH, nkn, nvn);
+        // scores of heads hu, hu + 2 for token n of each unit (as qk_kernel, summed over
+        // the row's blocks), -inf past the range; the units' packed value codes into
+        // their tiles (row n, block jb, bytes 4 BITS part ..)
+        float su[DEPTH], sv[DEPTH], nvd[DEPTH][M];
         float bu = -__builtin_inff(), bv = -__builtin_inff(), bn = 0.0f;
 #pragma unroll
-        for (int d = 0; d < kAttnDepth; ++d) {
+        for (int d = 0; d < DEPTH; ++d) {
             uint32_t *rt = raw_base + (d * kWavesPerGroup + wave) * kRawWords;
+            f4_t sc = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            float nmax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < LW; ++i)
-                rt[n * 12 + part * LW + i] = wv[d][i];
-            const f4_t Du = qk_unit<BITS>(A, wk[d], tcopy);
-            const uint16_t nk16 = (uint16_t)__shfl((int)nkc, 16 * d + (int)n, 64);
-            const uint16_t nv16 = (uint16_t)__shfl((int)nvc, 16 * d + (int)n, 64);
-            const f4_t sc = Du * (float)__builtin_bit_cast(_Float16, nk16);
+            for (int jb = 0; jb < M; ++jb) {
+#pragma unroll
+                for (int i = 0; i < LW; ++i)
+                    rt[n * RW + 12 * jb + part * LW + i] = wv[d][jb][i];
+                const int src = (16 * d + (int)n) * M + jb;   // the lane holding this norm
+                const uint16_t nk16 = (uint16_t)__shfl((int)nkc, src, 64);
+                const uint16_t nv16 = (uint16_t)__shfl((int)nvc, src, 64);
+                f4_t Du;
+                if constexpr (M == 1) {
+                    Du = qk_unit<BITS>(A, wk[d][0], tcopy);
+                } else {
+                    h8_t Aj[8];
+                    load_a(jb, Aj);
+                    Du = qk_unit<BITS>(Aj, wk[d][jb], tcopy);
+                }
+                sc += Du * (float)__builtin_bit_cast(_Float16, nk16);
+                nvd[d][jb] = (float)__builtin_bit_cast(_Float16, nv16);
+                nmax = __builtin_fmaxf(nmax, nvd[d][jb]);
+            }
             float s0 = sc[0], s1 = sc[1], s2 = sc[2], s3 = sc[3];
             swap32(s0, s1);
             swap32(s2, s3);
             const bool live = first + 16u * (k0 + d) + n < last;
             su[d] = live ? (s0 + s1) * pw_u : -__builtin_inff();
             sv[d] = live ? (s2 + s3) * pw_v : -__builtin_inff();
-            nvd[d] = (float)__builtin_bit_cast(_Float16, nv16);
             bu = __builtin_fmaxf(bu, su[d]);
             bv = __builtin_fmaxf(bv, sv[d]);
-            bn = __builtin_fmaxf(bn, live ? nvd[d] : 0.0f);
-            fetch(k0 + kAttnDepth + d, wk[d], wv[d]);
+            bn = __builtin_fmaxf(bn, live ? nmax : 0.0f);
+            fetch(k0 + DEPTH + d, wk[d], wv[d]);
         }
-        // online softmax over the batch's 64 rows (unit k0 holds a live row, so the
+        // online softmax over the batch's 64 / M rows (unit k0 holds a live row, so the
         // maxima are finite); the value-norm exponent follows the largest norm so far
         const float mu = __builtin_fmaxf(m_u, row16_max(bu));
         const float mv = __builtin_fmaxf(m_v, row16_max(bv));
@@ -1451,13 +1481,16 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
         const int En = max(E, __builtin_amdgcn_readfirstlane(eu));
         float ru = 0.0f, rv = 0.0f;
 #pragma unroll
-        for (int d = 0; d < kAttnDepth; ++d) {
+        for (int d = 0; d < DEPTH; ++d) {
             const float pu = exp2_fast(su[d] - mu), pv = exp2_fast(sv[d] - mv);
             ru += pu;
             rv += pv;
-            uint32_t *pt = pt_base + (d * kWavesPerGroup + wave) * (kQkHeads * 16);
-            pt[hu * 16 + n] = split_pack(ldexpf(pu * nvd[d], kAttnWExp - En));
-            pt[(hu + 2) * 16 + n] = split_pack(ldexpf(pv * nvd[d], kAttnWExp - En));
+#pragma unroll
+            for (int jb = 0; jb < M; ++jb) {
+                uint32_t *pt = pt_base + ((d * M + jb) * kWavesPerGroup + wave) * (kQkHeads * 16);
+                pt[hu * 16 + n] = split_pack(ldexpf(pu * nvd[d][jb], kAttnWExp - En));
+                pt[(hu + 2) * 16 + n] = split_pack(ldexpf(pv * nvd[d][jb], kAttnWExp - En));
+            }
         }
         l_u = l_u * au + row16_sum(ru);
         l_v = l_v * av + row16_sum(rv);
@@ -1476,44 +1509,49 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
                 const float2 f2 = *(const float2 *)(ft + 4 * hs + 2 * (part & 1u));
                 const f4_t f4 = f4_t{f2.x, f2.x, f2.y, f2.y};
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[hs][c] = acc[hs][c] * f4;
+                for (int jb = 0; jb < M; ++jb)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[jb][hs][c] = acc[jb][hs][c] * f4;
             }
         }
         E = En;
         wave_lds_sync();   // weights and code tiles complete
 #pragma unroll
-        for (int d = 0; d < kAttnDepth; ++d) {
+        for (int d = 0; d < DEPTH; ++d) {
             const uint32_t *rt = raw_base + (d * kWavesPerGroup + wave) * kRawWords;
-            const uint32_t *pt = pt_base + (d * kWavesPerGroup + wave) * (kQkHeads * 16);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                // B: positions 8 n + 2 c, + 1 of tokens 8 kb + 2 part, + 1 (one lookup each)
-                uint64_t ent[2][4];
+            for (int jb = 0; jb < M; ++jb) {
+                const uint32_t *pt = pt_base + ((d * M + jb) * kWavesPerGroup + wave) * (kQkHeads * 16);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t *row = rt + (8 * kb + 2 * part + j) * 12 + dA;
-                    const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
+                for (int kb = 0; kb < 2; ++kb) {
+                    // B: positions 8 n + 2 c, + 1 of tokens 8 kb + 2 part, + 1 (one lookup each)
+                    uint64_t ent[2][4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const uint32_t e = __builtin_amdgcn_ubfe(f, 2 * BITS * c, 2 * BITS);
-                        ent[j][c] = lds_load<uint64_t>(lshl_add<8>(e, vcopy));
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t *row = rt + (8 * kb + 2 * part + j) * RW + 12 * jb + dA;
+                        const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint32_t e = __builtin_amdgcn_ubfe(f, 2 * BITS * c, 2 * BITS);
+                            ent[j][c] = lds_load<uint64_t>(lshl_add<8>(e, vcopy));
+                        }
                     }
-                }
 #pragma unroll
-                for (int hs = 0; hs < NHS; ++hs) {
-                    // A: the weights of head 4 hs + a_hh, tokens 8 kb + 2 part, + 1
-                    const uint2 x = *(const uint2 *)(pt + (4 * hs + a_hh) * 16 + 8 * kb + 2 * part);
-                    const uint32_t a0 = __builtin_amdgcn_perm(x.x, x.x, a_sel);
-                    const uint32_t a1 = __builtin_amdgcn_perm(x.y, x.y, a_sel);
-                    const u4_t av = u4_t{a0, a0, a1, a1};
+                    for (int hs = 0; hs < NHS; ++hs) {
+                        // A: the weights of head 4 hs + a_hh, tokens 8 kb + 2 part, + 1
+                        const uint2 x = *(const uint2 *)(pt + (4 * hs + a_hh) * 16 + 8 * kb + 2 * part);
+                        const uint32_t a0 = __builtin_amdgcn_perm(x.x, x.x, a_sel);
+                        const uint32_t a1 = __builtin_amdgcn_perm(x.y, x.y, a_sel);
+                        const u4_t av = u4_t{a0, a0, a1, a1};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const u4_t bv = u4_t{(uint32_t)ent[0][c], (uint32_t)(ent[0][c] >> 32),
-                                             (uint32_t)ent[1][c], (uint32_t)(ent[1][c] >> 32)};
-                        acc[hs][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(h8_t, av), __builtin_bit_cast(h8_t, bv), acc[hs][c],
-                            0, 0, 0);
+                        for (int c = 0; c < 4; ++c) {
+                            const u4_t bv = u4_t{(uint32_t)ent[0][c], (uint32_t)(ent[0][c] >> 32),
+                                                 (uint32_t)ent[1][c], (uint32_t)(ent[1][c] >> 32)};
+                            acc[jb][hs][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(h8_t, av), __builtin_bit_cast(h8_t, bv),
+                                acc[jb][hs][c], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -1524,27 +1562,30 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
 
     // this wave's state into LDS (over the tables), then merged: rows r (hi) and r + 8
     // (lo) of acc sit in lanes l and l + 32; after the combine lane l holds positions
-    // 8 n .. 8 n + 7 of head 4 s + hv
+    // 8 n .. 8 n + 7 of block jb of head 4 s + hv
     __syncthreads();   // every wave is done with the tables
-    float *mg = (float *)smem;   // [wave][head][acc[128], m, l, -, -]
+    float *mg = (float *)smem;   // [wave][head][acc[128 M], m, l, -, -]
 #pragma unroll
-    for (int hs = 0; hs < NHS; ++hs) {
-        float o[8];
+    for (int jb = 0; jb < M; ++jb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float a0 = acc[hs][c][0], a1 = acc[hs][c][1], a2 = acc[hs][c][2], a3 = acc[hs][c][3];
-            swap32(a0, a2);
-            swap32(a1, a3);
-            o[2 * c] = ldexpf(a0 + a2, E - kAttnWExp);
-            o[2 * c + 1] = ldexpf(a1 + a3, E - kAttnWExp);
+        for (int hs = 0; hs < NHS; ++hs) {
+            float o[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float a0 = acc[jb][hs][c][0], a1 = acc[jb][hs][c][1];
+                float a2 = acc[jb][hs][c][2], a3 = acc[jb][hs][c][3];
+                swap32(a0, a2);
+                swap32(a1, a3);
+                o[2 * c] = ldexpf(a0 + a2, E - kAttnWExp);
+                o[2 * c + 1] = ldexpf(a1 + a3, E - kAttnWExp);
+            }
+            float *r = mg + (wave * kQkHeads + 4 * hs + hv) * REC + kBlock * jb + 8 * n;
+            *(float4 *)r = float4{o[0], o[1], o[2], o[3]};
+            *(float4 *)(r + 4) = float4{o[4], o[5], o[6], o[7]};
         }
-        float *r = mg + (wave * kQkHeads + 4 * hs + hv) * kAttnRec + 8 * n;
-        *(float4 *)r = float4{o[0], o[1], o[2], o[3]};
-        *(float4 *)(r + 4) = float4{o[4], o[5], o[6], o[7]};
-    }
     if (n == 0) {
-        float *ru = mg + (wave * kQkHeads + hu) * kAttnRec + kBlock;
-        float *rv = mg + (wave * kQkHeads + hu + 2) * kAttnRec + kBlock;
+        float *ru = mg + (wave * kQkHeads + hu) * REC + kBlock * M;
+        float *rv = mg + (wave * kQkHeads + hu + 2) * REC + kBlock * M;
         ru[0] = m_u;
         ru[1] = l_u;
         rv[0] = m_v;
@@ -1552,29 +1593,37 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     }
     __syncthreads();
     {
-        // thread -> head threadIdx / 32, values 4 (threadIdx % 32) .. + 3
+        // thread -> head threadIdx / 32, values 4 (threadIdx % 32) .. + 3 of every block
         const uint32_t h = threadIdx.x >> 5, v0 = 4u * (threadIdx.x & 31u);
-        float M = -__builtin_inff();
+        float Mx = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w)
-            M = __builtin_fmaxf(M, mg[(w * kQkHeads + h) * kAttnRec + kBlock]);
-        float L = 0.0f, a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            Mx = __builtin_fmaxf(Mx, mg[(w * kQkHeads + h) * REC + kBlock * M]);
+        float L = 0.0f, a[M][4];
+#pragma unroll
+        for (int jb = 0; jb < M; ++jb)
+            a[jb][0] = a[jb][1] = a[jb][2] = a[jb][3] = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) {
-            const float *r = mg + (w * kQkHeads + h) * kAttnRec;
-            const float f = r[kBlock] == -__builtin_inff() ? 0.0f : exp2_fast(r[kBlock] - M);
-            L += f * r[kBlock + 1];
-            const float4 x = *(const float4 *)(r + v0);
-            a[0] += f * x.x;
-            a[1] += f * x.y;
-            a[2] += f * x.z;
-            a[3] += f * x.w;
+            const float *r = mg + (w * kQkHeads + h) * REC;
+            const float f = r[kBlock * M] == -__builtin_inff() ? 0.0f : exp2_fast(r[kBlock * M] - Mx);
+            L += f * r[kBlock * M + 1];
+#pragma unroll
+            for (int jb = 0; jb < M; ++jb) {
+                const float4 x = *(const float4 *)(r + kBlock * jb + v0);
+                a[jb][0] += f * x.x;
+                a[jb][1] += f * x.y;
+                a[jb][2] += f * x.z;
+                a[jb][3] += f * x.w;
+            }
         }
         if (h < nh) {
-            float *rec = work + (((size_t)b * Hq + h0 + h) * nparts + blockIdx.y) * kAttnRec;
-            *(float4 *)(rec + 4 + v0) = float4{a[0], a[1], a[2], a[3]};
+            float *rec = work + (((size_t)b * Hq + h0 + h) * nparts + blockIdx.y) * REC;
+#pragma unroll
+            for (int jb = 0; jb < M; ++jb)
+                *(float4 *)(rec + 4 + kBlock * jb + v0) = float4{a[jb][0], a[jb][1], a[jb][2], a[jb][3]};
             if (v0 == 0) {
-                rec[0] = M;
+                rec[0] = Mx;
                 rec[1] = L;
             }
         }
@@ -1582,60 +1631,76 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
 }
 
 // One workgroup per (sequence, query head): merge the chunks' partials (wave w takes
-// chunks w, w + 4, ...; lane l values l and 64 + l), add the four waves, transform
-// once and divide by 128 l.
+// chunks w, w + 4, ...; lane l values l and 64 + l of every block), add the four waves,
+// transform each block once and divide by 128 l.
+template <int M>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ work,
                                                            float *__restrict__ out,
                                                            uint32_t nparts, Signs sg)
 {
-    __shared__ float red[kWavesPerGroup][kBlock + 1];
+    constexpr int REC = attn_rec(M);
+    __shared__ float red[kWavesPerGroup][kBlock * M + 1];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t bh = blockIdx.x;
-    const float *rec = work + (size_t)bh * nparts * kAttnRec;
+    const float *rec = work + (size_t)bh * nparts * REC;
     // the largest running max over all chunks (every wave computes it)
-    float M = -__builtin_inff();
+    float Mx = -__builtin_inff();
     for (uint32_t p = lane; p < nparts; p += 64)
-        M = __builtin_fmaxf(M, rec[(size_t)p * kAttnRec]);
+        Mx = __builtin_fmaxf(Mx, rec[(size_t)p * REC]);
 #pragma unroll
     for (int h = 32; h >= 1; h >>= 1)
-        M = __builtin_fmaxf(M, __shfl_xor(M, h, 64));
-    float L = 0.0f, a = 0.0f, c = 0.0f;
+        Mx = __builtin_fmaxf(Mx, __shfl_xor(Mx, h, 64));
+    float L = 0.0f, a[M], c[M];
+#pragma unroll
+    for (int jb = 0; jb < M; ++jb)
+        a[jb] = c[jb] = 0.0f;
 #pragma unroll 4
     for (uint32_t p = wave; p < nparts; p += kWavesPerGroup) {
-        const float *r = rec + (size_t)p * kAttnRec;
-        const float w = exp2_fast(r[0] - M);   // every chunk holds a row: r[0] is finite
+        const float *r = rec + (size_t)p * REC;
+        const float w = exp2_fast(r[0] - Mx);   // every chunk holds a row: r[0] is finite
         L += w * r[1];
-        a += w * r[4 + lane];
-        c += w * r[68 + lane];
+#pragma unroll
+        for (int jb = 0; jb < M; ++jb) {
+            a[jb] += w * r[4 + kBlock * jb + lane];
+            c[jb] += w * r[68 + kBlock * jb + lane];
+        }
     }
-    red[wave][lane] = a;
-    red[wave][64 + lane] = c;
+#pragma unroll
+    for (int jb = 0; jb < M; ++jb) {
+        red[wave][kBlock * jb + lane] = a[jb];
+        red[wave][kBlock * jb + 64 + lane] = c[jb];
+    }
     if (lane == 0)
-        red[wave][kBlock] = L;
+        red[wave][kBlock * M] = L;
     __syncthreads();
     if (wave != 0)
         return;
-    a = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    c = red[0][64 + lane] + red[1][64 + lane] + red[2][64 + lane] + red[3][64 + lane];
-    L = red[0][kBlock] + red[1][kBlock] + red[2][kBlock] + red[3][kBlock];
-    // H: span 64 in-lane, spans 32..1 across lanes
-    const float s0 = a + c;
-    c = a - c;
-    a = s0;
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) {
-        const float pa = __shfl_xor(a, h, 64), pc = __shfl_xor(c, h, 64);
-        const bool up = (lane & (uint32_t)h) != 0u;
-        a = up ? pa - a : a + pa;
-        c = up ? pc - c : c + pc;
-    }
-    // D H acc / (128 l): the randomised rotation's signs flip the output positions
+    L = red[0][kBlock * M] + red[1][kBlock * M] + red[2][kBlock * M] + red[3][kBlock * M];
     const float inv = 1.0f / (128.0f * L);
-    const uint32_t ua = __builtin_bit_cast(uint32_t, a * inv) ^ sign_mask_f32(sg, lane);
-    const uint32_t uc = __builtin_bit_cast(uint32_t, c * inv) ^ sign_mask_f32(sg, 64u + lane);
-    out[(size_t)bh * kBlock + lane] = __builtin_bit_cast(float, ua);
-    out[(size_t)bh * kBlock + 64 + lane] = __builtin_bit_cast(float, uc);
+#pragma unroll
+    for (int jb = 0; jb < M; ++jb) {
+        const uint32_t o = kBlock * jb;
+        float x = red[0][o + lane] + red[1][o + lane] + red[2][o + lane] + red[3][o + lane];
+        float y = red[0][o + 64 + lane] + red[1][o + 64 + lane] + red[2][o + 64 + lane] +
+                  red[3][o + 64 + lane];
+        // H: span 64 in-lane, spans 32..1 across lanes
+        const float s0 = x + y;
+        y = x - y;
+        x = s0;
+#pragma unroll
+        for (int h = 32; h >= 1; h >>= 1) {
+            const float px = __shfl_xor(x, h, 64), py = __shfl_xor(y, h, 64);
+            const bool up = (lane & (uint32_t)h) != 0u;
+            x = up ? px - x : x + px;
+            y = up ? py - y : y + py;
+        }
+        // D H acc / (128 l): the randomised rotation's signs flip the output positions
+        const uint32_t ux = __builtin_bit_cast(uint32_t, x * inv) ^ sign_mask_f32(sg, lane);
+        const uint32_t uy = __builtin_bit_cast(uint32_t, y * inv) ^ sign_mask_f32(sg, 64u + lane);
+        out[(size_t)bh * kBlock * M + o + lane] = __builtin_bit_cast(float, ux);
+        out[(size_t)bh * kBlock * M + o + 64 + lane] = __builtin_bit_cast(float, uy);
+    }
 }
 
 // ---------------------------------------------------------------- interleaved records
@@ -1940,11 +2005,11 @@ int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *
 
 // Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
 // device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
-// of kAttnDepth units per wave, at most 65535 chunks.
-int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+// of attn_depth(m) units per wave, at most 65535 chunks.
+int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq, int64_t m)
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
-    const int64_t step = (int64_t)kWavesPerGroup * 16 * kAttnDepth;
+    const int64_t step = (int64_t)kWavesPerGroup * 16 * attn_depth((int)m);
     const int64_t round = 256 * attn_groups_per_cu(bits);
     int64_t rows = (T * B * Hkv * passes + round - 1) / round;
     rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
@@ -1972,44 +2037,51 @@ void *attn_scratch()
     return p;
 }
 
-int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq)
+int64_t attn_workspace_bytes(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq, int64_t m)
 {
-    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq);
+    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq, m);
     const int64_t chunks = (T + rows - 1) / rows;
-    return B * Hq * chunks * kAttnRec * (int64_t)sizeof(float);
+    return B * Hq * chunks * attn_rec((int)m) * (int64_t)sizeof(float);
 }
 
 int launch_attn(int bits, const Signs &sg, const void *k_codes, const void *k_norms,
                 const void *v_codes, const void *v_norms, int64_t B, int64_t Hkv, int64_t Tc,
-                int64_t T, const void *q, int64_t Hq, float scale, float *out, void *work,
-                void *stream)
+                int64_t m, int64_t T, const void *q, int64_t Hq, float scale, float *out,
+                void *work, void *stream)
 {
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
-    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq);
+    const int64_t rows = attn_chunk_rows(bits, B, Hkv, T, Hq, m);
     const int64_t chunks = (T + rows - 1) / rows;
     const uint32_t nparts = (uint32_t)chunks;
     dim3 grid((uint32_t)(B * Hkv * passes), (uint32_t)chunks), block(256);
-    if (bits == 3)
-        launch_kernel((G > 4 ? attn_partial_kernel<3, 2> : attn_partial_kernel<3, 1>), grid,
-                      block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
-                      (const uint8_t *)v_codes, (const uint16_t *)v_norms,
-                      (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
-                      (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                      scale, *cb, sg);
-    else
-        launch_kernel((G > 4 ? attn_partial_kernel<2, 2> : attn_partial_kernel<2, 1>), grid,
-                      block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
-                      (const uint8_t *)v_codes, (const uint16_t *)v_norms,
-                      (const uint16_t *)q, (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T,
-                      (uint32_t)G, (uint32_t)Hq, (uint32_t)passes, (uint32_t)rows, nparts,
-                      scale, *cb, sg);
+    auto partial = [&](auto kern) {
+        launch_kernel(kern, grid, block, 0, s, (const uint8_t *)k_codes, (const uint16_t *)k_norms,
+                      (const uint8_t *)v_codes, (const uint16_t *)v_norms, (const uint16_t *)q,
+                      (float *)work, (uint32_t)Hkv, Tc, (uint32_t)T, (uint32_t)G, (uint32_t)Hq,
+                      (uint32_t)passes, (uint32_t)rows, nparts, scale, *cb, sg);
+    };
+    if (m == 1) {
+        if (bits == 3)
+            G > 4 ? partial(attn_partial_kernel<3, 2, 1>) : partial(attn_partial_kernel<3, 1, 1>);
+        else
+            G > 4 ? partial(attn_partial_kernel<2, 2, 1>) : partial(attn_partial_kernel<2, 1, 1>);
+    } else {
+        if (bits == 3)
+            G > 4 ? partial(attn_partial_kernel<3, 2, 2>) : partial(attn_partial_kernel<3, 1, 2>);
+        else
+            G > 4 ? partial(attn_partial_kernel<2, 2, 2>) : partial(attn_partial_kernel<2, 1, 2>);
+    }
     int e = (int)hipGetLastError();
     if (e)
         return e;
-    launch_kernel(attn_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
-                  (const float *)work, out, nparts, sg);
+    if (m == 1)
+        launch_kernel(attn_combine_kernel<1>, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
+                      (const float *)work, out, nparts, sg);
+    else
+        launch_kernel(attn_combine_kernel<2>, dim3((uint32_t)(B * Hq)), dim3(256), 0, s,
+                      (const float *)work, out, nparts, sg);
     return (int)hipGetLastError();
 }
 

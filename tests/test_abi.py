@@ -137,7 +137,7 @@ def test_qk_validation(L):
 
 
 def test_attn_workspace_bytes():
-    """Depends on the sizes only; 132 floats (m, l, two spare, 128 values) per partial,
+    """Depends on the sizes only; 4 + D floats (m, l, two spare, D values) per partial,
     one partial per row chunk of every (sequence, query head)."""
     ws = tq.tq_attn_workspace_bytes
     assert ws(3, 0, 8, 32768, 128, 32768, 32) == 0
@@ -145,8 +145,11 @@ def test_attn_workspace_bytes():
     assert n16 > 0 and n16 % (16 * 32 * 132 * 4) == 0
     n1 = ws(2, 1, 8, 32768, 128, 32768, 32)
     assert n1 > 0 and n1 % (32 * 132 * 4) == 0
-    with pytest.raises(tq.TQError):
-        ws(3, 1, 8, 100, 256, 100, 32)       # D != 128
+    n256 = ws(2, 32, 4, 32768, 256, 32768, 16)
+    assert n256 > 0 and n256 % (32 * 16 * 260 * 4) == 0
+    for D in (384, 512, 100):
+        with pytest.raises(tq.TQError):
+            ws(3, 1, 8, 100, D, 100, 32)         # D not 128 or 256
     with pytest.raises(tq.TQError):
         ws(3, 1, 8, 100, 128, 0, 32)         # no rows
     with pytest.raises(tq.TQError):
@@ -190,7 +193,8 @@ def test_attn_validation(L):
 
     assert call(t=1) == E_TYPE
     assert call(Hq=7) == E_SHAPE
-    assert call(D=256) == E_SHAPE
+    assert call(D=384) == E_SHAPE
+    assert call(D=256) == E_WORKSPACE      # valid sizes; the workspace is the head_dim-128 one
     assert call(T=0) == E_SHAPE
     assert call(T=9) == E_RANGE
     assert call(vc=None) == E_NULL
@@ -240,7 +244,7 @@ def test_rot_entry_points_validate_like_the_plain_ones(L):
         assert q(3, signs, _p(C), _p(N), 1, 2, 8, 128, 8, _p(Q), 3, ctypes.c_float(1.0), S4, None) == E_SHAPE
         assert q(3, signs, _p(C), _p(N), 1, 2, 8, 128, 9, _p(Q), 4, ctypes.c_float(1.0), S4, None) == E_RANGE
         a = L.tq_attn_decode_rot
-        assert a(3, signs, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 8, 256, 8,
+        assert a(3, signs, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 8, 384, 8,
                  _p(Q), 4, ctypes.c_float(1.0), S4, _p(0x60000000), 1 << 20, None) == E_SHAPE
         assert a(3, signs, _p(C), _p(N), _p(C + 0x1000000), _p(N + 0x1000000), 1, 2, 8, 128, 8,
                  _p(Q), 4, ctypes.c_float(1.0), S4, _p(0x60000000), 0, None) == E_WORKSPACE
@@ -324,7 +328,7 @@ def test_attn_noalloc_validation(L):
     sc = ctypes.c_float(0.1)
     K2, N2 = C + 0x1000000, N + 0x1000000
     assert f(4, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_TYPE
-    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 256, 16, _p(Q), 8, sc, _p(S), None) == E_SHAPE
+    assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 384, 16, _p(Q), 8, sc, _p(S), None) == E_SHAPE
     assert f(3, None, _p(C), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 17, _p(Q), 8, sc, _p(S), None) == E_RANGE
     assert f(3, None, None, _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_NULL
     assert f(3, None, _p(C + 8), _p(N), _p(K2), _p(N2), 1, 2, 16, 128, 16, _p(Q), 8, sc, _p(S), None) == E_ALIGN

@@ -205,25 +205,25 @@ def test_qk_query_magnitudes(bits):
 
 # ---------------------------------------------------------------- decode attention
 
-def _attn_case(bits, B, Hkv, G, Tc, T, seed, q_mul=1.0, scale=None, v_mul=1.0, zero_rows=()):
-    k = _rand_kv(seed, B, Hkv, Tc, 128)
-    v = _rand_kv(seed + 7, B, Hkv, Tc, 128)
+def _attn_case(bits, B, Hkv, G, Tc, T, seed, q_mul=1.0, scale=None, v_mul=1.0, zero_rows=(), D=128):
+    k = _rand_kv(seed, B, Hkv, Tc, D)
+    v = _rand_kv(seed + 7, B, Hkv, Tc, D)
     v = (v.double() * v_mul).half()
     for t in zero_rows:
         v[:, :, t] = 0
     kc, kn = _gpu_encode(bits, k, Tc, 0)
     vc, vn = _gpu_encode(bits, v, Tc, 0)
-    q = (gen.queries(seed + 1, B, Hkv * G, 128).double() * q_mul).half()
+    q = (gen.queries(seed + 1, B, Hkv * G, D).double() * q_mul).half()
     assert bool(torch.isfinite(q).all()) and bool(torch.isfinite(v).all())
-    scale = 1.0 / math.sqrt(128) if scale is None else scale
-    out = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device="cuda")
     tq.tq_attn_decode(bits, kc, kn, vc, vn, q.cuda(), scale, out, T=T)
     torch.cuda.synchronize()
     vcn, vnn = vc.cpu().numpy(), vn.cpu().numpy()
     ref = oracle.attn_decode(bits, kc.cpu().numpy(), kn.cpu().numpy(), vcn, vnn, q.numpy(), scale, T=T)
     vhat = oracle.decode_blocks(bits, vcn[:, :, :T].reshape(-1, 16 * bits), vnn[:, :, :T].reshape(-1))[0]
     vmax = np.repeat(np.abs(vhat).reshape(B, Hkv, -1).max(axis=-1), G, axis=1)
-    return check_attn(out.cpu().numpy(), ref, vmax, T, f"attn bits={bits} B={B} Hkv={Hkv} G={G} T={T}")
+    return check_attn(out.cpu().numpy(), ref, vmax, T, f"attn bits={bits} B={B} Hkv={Hkv} G={G} T={T} D={D}")
 
 
 @pytest.mark.parametrize("bits", [3, 2])
@@ -239,6 +239,32 @@ def _attn_case(bits, B, Hkv, G, Tc, T, seed, q_mul=1.0, scale=None, v_mul=1.0, z
 def test_attn_decode(bits, case):
     B, Hkv, G, Tc, T = case
     print(_attn_case(bits, B, Hkv, G, Tc, T, seed=41 + G + T % 97))
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("case", [
+    (1, 2, 4, 100, 97),      # GQA group 4, ragged T < Tc
+    (2, 1, 8, 40, 33),       # group 8: one full pass
+    (1, 1, 12, 300, 300),    # group 12: passes of eight and four heads
+    (1, 3, 1, 70, 70),       # no grouping
+    (1, 2, 2, 1, 1),         # one row: the output is that row's value
+    (1, 2, 4, 5000, 4999),   # many row chunks and waves, ragged last unit
+    (3, 2, 4, 2000, 1500),   # several sequences, T well below Tc
+])
+def test_attn_decode_head_dim_256(bits, case):
+    """head_dim 256 (two 128-blocks per row, each with its own norm; section
+    "実モデルでの数値"): the fused attention against the oracle."""
+    B, Hkv, G, Tc, T = case
+    print(_attn_case(bits, B, Hkv, G, Tc, T, seed=61 + G + T % 89, D=256))
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_attn_decode_head_dim_256_extremes(bits):
+    """head_dim 256 under a peaked softmax, value norms far from the usual and rows of
+    zeros in the values that carry the largest weights."""
+    print(_attn_case(bits, 1, 2, 4, 600, 600, seed=71, scale=2.0, D=256))
+    print(_attn_case(bits, 1, 2, 4, 600, 590, seed=72, v_mul=1e-4, D=256))
+    print(_attn_case(bits, 1, 2, 4, 300, 300, seed=73, scale=2.0, zero_rows=range(1, 300, 2), D=256))
 
 
 @pytest.mark.parametrize("bits", [3, 2])

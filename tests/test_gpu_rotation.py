@@ -120,20 +120,22 @@ def test_rot_qk(bits, case):
 
 @pytest.mark.parametrize("bits", [3, 2])
 @pytest.mark.parametrize("case", [
-    (1, 2, 4, 100, 97),      # GQA group 4, ragged T < Tc
-    (2, 1, 8, 40, 33),       # group 8: two head sets
-    (1, 2, 4, 5000, 4999),   # many row chunks and waves
+    (1, 2, 4, 100, 97, 128),      # GQA group 4, ragged T < Tc
+    (2, 1, 8, 40, 33, 128),       # group 8: two head sets
+    (1, 2, 4, 5000, 4999, 128),   # many row chunks and waves
+    (1, 2, 4, 3000, 2999, 256),   # head_dim 256: the signs apply to each block
+    (2, 1, 8, 40, 33, 256),
 ])
 def test_rot_attention(bits, case):
-    B, Hkv, G, Tc, T = case
+    B, Hkv, G, Tc, T, D = case
     d = _signs(300 + T % 97)
-    k = _rand_kv(51 + G, B, Hkv, Tc, 128)
-    v = gen.kv_tensor(52 + G, "V", gen.KVSpec(n_outliers=3, row_scale=True), B, Hkv, Tc, 128)
+    k = _rand_kv(51 + G, B, Hkv, Tc, D)
+    v = gen.kv_tensor(52 + G, "V", gen.KVSpec(n_outliers=3, row_scale=True), B, Hkv, Tc, D)
     kc, kn = _encode(bits, k, Tc, 0, d)
     vc, vn = _encode(bits, v, Tc, 0, d)
-    q = gen.queries(53 + G, B, Hkv * G, 128)
-    scale = 1.0 / math.sqrt(128)
-    out = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    q = gen.queries(53 + G, B, Hkv * G, D)
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device="cuda")
     tq.tq_attn_decode(bits, kc, kn, vc, vn, q.cuda(), scale, out, T=T, signs=d)
     torch.cuda.synchronize()
     vcn, vnn = vc.cpu().numpy(), vn.cpu().numpy()

@@ -18,11 +18,11 @@ pytestmark = pytest.mark.gpu
 SPEC = gen.KVSpec(n_outliers=3, row_scale=True)
 
 
-def _cache(bits, seed, name, B, Hkv, T):
-    x = torch.empty((B, Hkv, T, 128), dtype=torch.float16, device="cuda")
+def _cache(bits, seed, name, B, Hkv, T, D=128):
+    x = torch.empty((B, Hkv, T, D), dtype=torch.float16, device="cuda")
     for b in range(B):
-        x[b] = gen.kv_layer(seed, name, SPEC, b, Hkv, T, 128, device="cuda")
-    codes, norms = tq.empty_cache(bits, B, Hkv, T, 128, "cuda")
+        x[b] = gen.kv_layer(seed, name, SPEC, b, Hkv, T, D, device="cuda")
+    codes, norms = tq.empty_cache(bits, B, Hkv, T, D, "cuda")
     tq.tq_encode(bits, x, codes, norms, 0)
     return codes, norms
 
@@ -30,10 +30,10 @@ def _cache(bits, seed, name, B, Hkv, T):
 def _noalloc_c_abi(bits, signs, kc, kn, vc, vn, q, scale, out, T):
     """Direct ctypes call of the C entry point (NULL stream: the default stream)."""
     B, Hkv, Tc = kc.shape[:3]
-    Hq = q.shape[1]
+    Hq, D = q.shape[1], q.shape[2]
     w = None if signs is None else tq.sign_words(signs)
     return tq.lib().tq_attn_decode_noalloc(bits, w, kc.data_ptr(), kn.data_ptr(), vc.data_ptr(),
-                                           vn.data_ptr(), B, Hkv, Tc, 128, T, q.data_ptr(), Hq,
+                                           vn.data_ptr(), B, Hkv, Tc, D, T, q.data_ptr(), Hq,
                                            ctypes.c_float(scale), out.data_ptr(), None)
 
 
@@ -42,15 +42,17 @@ def test_noalloc_attention_equals_workspace_attention(bits):
     torch.cuda.set_device(0)
     scale = 1.0 / math.sqrt(128)
     signs = np.where(np.random.default_rng(9).random(128) < 0.5, -1.0, 1.0)
-    # two calls in a row, the second one smaller (fewer sequences, heads and rows)
-    for i, (B, Hkv, G, Tc, T) in enumerate(((4, 8, 4, 8192, 8192), (2, 2, 4, 1200, 1000))):
-        kc, kn = _cache(bits, 30 + i, "K", B, Hkv, Tc)
-        vc, vn = _cache(bits, 30 + i, "V", B, Hkv, Tc)
-        q = gen.queries(40 + i, B, Hkv * G, 128, device="cuda")
-        need = tq.tq_attn_workspace_bytes(bits, B, Hkv, Tc, 128, T, Hkv * G)
+    # calls in a row, each one smaller than the one before (fewer sequences, heads and
+    # rows), head_dim 256 then 128
+    for i, (B, Hkv, G, Tc, T, D) in enumerate(((4, 8, 4, 8192, 8192, 256), (4, 8, 4, 8192, 8192, 128),
+                                               (2, 2, 4, 1200, 1000, 128))):
+        kc, kn = _cache(bits, 30 + i, "K", B, Hkv, Tc, D)
+        vc, vn = _cache(bits, 30 + i, "V", B, Hkv, Tc, D)
+        q = gen.queries(40 + i, B, Hkv * G, D, device="cuda")
+        need = tq.tq_attn_workspace_bytes(bits, B, Hkv, Tc, D, T, Hkv * G)
         assert 0 < need <= tq.TQ_ATTN_SCRATCH_BYTES
         for sg in (None, signs):
-            ref = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+            ref = torch.empty((B, Hkv * G, D), dtype=torch.float32, device="cuda")
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, ref, T=T, workspace=ws, signs=sg)
             out = torch.full_like(ref, float("nan"))
