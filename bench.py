@@ -27,7 +27,9 @@ Printed: one JSON line.  Outside the timed steps and not part of value:
   "records_14b"       the same turbo3 cache into interleaved 50-byte block records
                       and back;
   "head_dim_256"      turbo2 encode and decode of a whole head_dim-256 cache
-                      (32 layers x 4 kv heads x 32768 x 256, K and V);
+                      (32 layers x 4 kv heads x 32768 x 256, K and V), and the fused
+                      read over it (its K layers as 32 sequences, 16 query heads: q.K
+                      and the decode attention over the K and V layers);
   "decode_step"       the read path at the decode-step size (16 sequences, each with
                       turbo3 K and V caches [8, 32768, 128]): the append of K and V, q.K
                       of 32 query heads and the fused decode attention over the
@@ -69,10 +71,10 @@ def qk_bytes(B, Hkv, T_, m, Hq, bits) -> int:
     return B * Hkv * T_ * m * (16 * bits + 2) + B * Hq * T_ * 4 + B * Hq * m * 128 * 2
 
 
-def attn_bytes(B, Hkv, T_, Hq, bits) -> int:
-    """Algorithmic bytes of a decode attention over T_ rows (head_dim 128): the K and V
+def attn_bytes(B, Hkv, T_, Hq, bits, m=1) -> int:
+    """Algorithmic bytes of a decode attention over T_ rows (head_dim 128 m): the K and V
     codes and norms once, the fp16 queries and the fp32 outputs."""
-    return 2 * B * Hkv * T_ * (16 * bits + 2) + B * Hq * 128 * (2 + 4)
+    return 2 * B * Hkv * T_ * m * (16 * bits + 2) + B * Hq * 128 * m * (2 + 4)
 
 
 def gbs(nbytes: float, us: float) -> float:
@@ -475,8 +477,10 @@ def decode_step(tq, gen, dev, stream, reps=20):
 
 def head_dim_256(tq, gen, dev, stream, reps=10):
     """turbo2 encode then decode of a whole head_dim-256 cache (32 layers x 4 kv heads x
-    32768 x 256, K and V as one [64, 4, 32768, 256] tensor, 4.3 GB of fp16); average of
-    `reps` back-to-back launches per op after ten untimed ones."""
+    32768 x 256, K and V as one [64, 4, 32768, 256] tensor, 4.3 GB of fp16), average of
+    `reps` back-to-back launches per op after ten untimed ones; then the fused read over
+    the same cache: its 32 K layers as a batch of 32 sequences (16 query heads, GQA 4),
+    q.K over all 32768 rows and the decode attention over the K and V layers."""
     import torch
     w = gen.WORKLOADS["head_dim_256"]
     bits = 2
@@ -498,7 +502,27 @@ def head_dim_256(tq, gen, dev, stream, reps=10):
         res[op] = {"us": round(us, 1), "bytes": nb, "GBps": round(gbs(nb, us), 1),
                    "frac_of_hbm_peak": round(gbs(nb, us) / HBM_PEAK_GBS, 4),
                    "Gvalues_per_s": round(nblk * 128 / (us * 1e-6) / 1e9, 1)}
-    del x, y, codes, norms
+    del x, y
+    B, Hkv, T_, D_, Hq = w.L, w.H, w.T, w.D, 4 * w.H
+    m = D_ // 128
+    kc, kn, vc, vn = codes[: w.L], norms[: w.L], codes[w.L:], norms[w.L:]
+    q = gen.queries(w.seed, B, Hq, D_, device=dev)
+    scores = torch.empty((B, Hq, T_), dtype=torch.float32, device=dev)
+    attn = torch.empty((B, Hq, D_), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attn_workspace_bytes(bits, B, Hkv, T_, D_, T_, Hq), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / math.sqrt(D_)
+    for name, nbytes, fn in (
+            ("qk", qk_bytes(B, Hkv, T_, m, Hq, bits),
+             lambda: tq.tq_qk_scores(bits, kc, kn, q, scale, scores)),
+            ("attn", attn_bytes(B, Hkv, T_, Hq, bits, m),
+             lambda: tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, attn, workspace=ws))):
+        us = time_back_to_back(fn, stream, reps)
+        res[name] = {"workload": f"the {B} K layers as {B} sequences x {Hkv} kv heads x {T_} rows x "
+                                 f"{D_}, {Hq} query heads" + (", V layers as values" if name == "attn" else ""),
+                     "us": round(us, 2), "bytes": nbytes, "GBps": round(gbs(nbytes, us), 1),
+                     "frac_of_hbm_peak": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4)}
+    del codes, norms, q, scores, attn, ws
     torch.cuda.empty_cache()
     return res
 

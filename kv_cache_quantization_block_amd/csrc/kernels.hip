@@ -738,6 +738,8 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
 constexpr int kQkDepth = 8;
 constexpr int kQkHeads = 8;         // query heads per pass
 constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)
+// with two blocks per row the query operands of both stay in registers: 3 groups per CU
+constexpr int qk_groups_per_cu(int64_t m) { return m == 2 ? 3 : kQkGroupsPerCu; }
 // turbo3: 64 two-value entries of 8 B, kLdsCopies8 copies (conflict-free);
 // turbo2: 256 four-value entries of 16 B, 8 copies (16 B lookups are served 16 lanes
 // per cycle, so lanes l and l + 8 may meet: the full 16 copies would take 64 KB and
@@ -940,24 +942,30 @@ __device__ __forceinline__ f4_t qk_unit(const h8_t (&A)[8], const uint32_t *w, u
     return D[0] + D[1];
 }
 
-// BITS: 2 or 3.  ONE_BLOCK: D == 128 (the query operands stay in registers).  A
-// workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head)
-// for up to eight query heads (pass blockIdx.x % passes).
-template <int BITS, bool ONE_BLOCK>
-__global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *__restrict__ k_codes,
+// BITS: 2 or 3.  MF: blocks per row of the batched path (1: D == 128, 2: D == 256; the
+// query operands of every block stay in registers), or 0: the general path for D = 128 m,
+// m >= 3 (query operands read from LDS per unit, per-unit norm loads and per-lane score
+// stores).  A
+// workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head) for up
+// to eight query heads (pass blockIdx.x % passes).
+template <int BITS, int MF>
+__global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uint8_t *__restrict__ k_codes,
                                                     const uint16_t *__restrict__ k_norms,
                                                     const uint16_t *__restrict__ q,
                                                     float *__restrict__ scores, uint32_t Hkv,
-                                                    int64_t Tc, uint32_t T, uint32_t m,
+                                                    int64_t Tc, uint32_t T, uint32_t m_arg,
                                                     uint32_t G, uint32_t Hq, uint32_t passes,
                                                     uint32_t tpg, float scale, Codebook cb,
                                                     Signs sg)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t qk_smem[];
+    constexpr bool FAST = MF > 0;              // the batched path
+    constexpr uint32_t MD = FAST ? MF : 1;     // (a divisor for the batched path's arithmetic)
     constexpr int NC = QkTable<BITS>::NC;
     constexpr int EB = QkTable<BITS>::EB;
     constexpr int CB = 16 * BITS;              // code bytes per block
     constexpr int LW = BITS;                   // code words per lane (32 codes)
+    const uint32_t m = FAST ? MD : m_arg;      // blocks per row
     uint8_t *table = qk_smem;
     _Float16 *qa = (_Float16 *)(qk_smem + qk_table_bytes(BITS));   // [m][16][128]
     float *pw_s = (float *)(qk_smem + qk_table_bytes(BITS) + (size_t)m * 16 * kBlock * 2);
@@ -985,15 +993,15 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     const uint32_t ngroups = first < last ? (last - first + 15u) / 16u : 0u;
     const uint32_t nunits = ngroups * m;
 
-    // Codes and raw norm of this lane's run of unit k.  Loads are unconditional (rows
-    // past the wave's range read valid rows of the chunk, at most row t_end - 1, and
-    // are never stored), so the prefetch is
-    // straight-line code; the group's base address is wave-uniform (scalar) and each
-    // lane adds a 32-bit offset.
+    // Codes (and, on the general path, the norm) of this lane's run of unit k.  Loads
+    // are unconditional (rows past the wave's range read valid rows of the chunk, at
+    // most row t_end - 1, and are never stored), so the prefetch is straight-line code;
+    // the group's base address is wave-uniform (scalar) and each lane adds a 32-bit
+    // offset.
     const uint32_t row_bytes = m * CB;
     auto fetch = [&](uint32_t k, uint32_t (&w)[LW], uint16_t &nr) {
-        const uint32_t gi = ONE_BLOCK ? k : k / m;
-        const uint32_t j = ONE_BLOCK ? 0u : k - gi * m;
+        const uint32_t gi = FAST ? k / MD : k / m;
+        const uint32_t j = k - gi * m;
         const uint32_t tb = min(first + gi * 16u, t_end - 1u);
         const uint32_t r = min(n, t_end - 1u - tb);
         const size_t blk0 = (row0 + tb) * m + j;
@@ -1002,22 +1010,23 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 #pragma unroll
         for (int i = 0; i < LW; ++i)
             w[i] = ld_stream(src + i);
-        if constexpr (!ONE_BLOCK)
-            nr = ld_stream((const uint16_t *)((const uint8_t *)(k_norms + blk0) + __umul24(r, 2u * m)));
+        if constexpr (!FAST)
+            nr = ld_stream(k_norms + blk0 + __umul24(r, m));
     };
-    // D == 128: the norms of a whole batch (kQkDepth groups = 128 contiguous rows) come
-    // in two loads, rows first + 16 k + lane and + 64, and each unit takes its row's
-    // norm from the lane that holds it; a separate small load per unit would cost the
-    // memory pipeline about as much as the unit's codes.
-    static_assert(!ONE_BLOCK || kQkDepth * 16 == 128, "two norm loads per batch");
+    // Batched path: a batch of kQkDepth units holds 128 (row, block) pairs, whose norms
+    // come in two loads (elements e0 + lane and e0 + 64 + lane from the batch's first
+    // row, clamped to the chunk's last element); each unit takes its pair's norm from
+    // the lane that holds it.  A separate small load per unit would cost the memory
+    // pipeline about as much as the unit's codes.
+    static_assert(kQkDepth * 16 == 128, "two norm loads per batch");
     auto fetch_norms = [&](uint32_t k, uint16_t &na, uint16_t &nb) {
-        const uint32_t ta = min(first + 16u * k + lane, t_end - 1u);
-        const uint32_t tb = min(first + 16u * k + 64u + lane, t_end - 1u);
-        na = ld_stream(k_norms + row0 + ta);
-        nb = ld_stream(k_norms + row0 + tb);
+        const size_t e0 = (row0 + first + 16u * (k / MD)) * MD;
+        const size_t emax = (row0 + t_end - 1u) * MD + (MD - 1u);
+        na = ld_stream(k_norms + min(e0 + lane, emax));
+        nb = ld_stream(k_norms + min(e0 + 64u + lane, emax));
     };
     uint16_t qpre[2][2] = {{0, 0}, {0, 0}};
-    if constexpr (ONE_BLOCK)   // the queries first: their wait does not cover the codes
+    if constexpr (MF == 1)   // the queries first: their wait does not cover the codes
         qk_load_queries(qpre, q, b, Hq, h0, nh, wave, lane);
     uint32_t wn[kQkDepth][LW];
     uint16_t nn[kQkDepth];
@@ -1027,7 +1036,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
         fetch(d, wn[d], nn[d]);
-    if constexpr (ONE_BLOCK)
+    if constexpr (FAST)
         fetch_norms(0, nna, nnb);
 
     __shared__ float lv[8];
@@ -1035,7 +1044,7 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     __syncthreads();
     qk_fill_table<BITS>(table, lv, (uint8_t *)qa);   // qa is written only below
 
-    qk_prepare_queries<ONE_BLOCK>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg, qpre);
+    qk_prepare_queries<MF == 1>(qa, pw_s, q, b, Hq, h0, nh, m, wave, lane, scale, sg, qpre);
     __syncthreads();
 
     // A operands of block j for this lane's row (lane % 16) and value run
@@ -1048,9 +1057,11 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             A[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
         }
     };
-    h8_t A[8];
-    if constexpr (ONE_BLOCK) {
-        load_a(0, A);
+    h8_t A[MD][8];
+    if constexpr (FAST) {
+#pragma unroll
+        for (int j = 0; j < (int)MD; ++j)
+            load_a(j, A[j]);
         __syncthreads();   // every wave holds its operands: qa is free for the score stages
     }
     // LDS address of this lane's table copy (entries are addressed as integers so that
@@ -1061,26 +1072,35 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
     const float pw_u = pw_s[hu], pw_v = pw_s[hu + 2];
     float* const out_u = scores + ((size_t)b * Hq + h0 + hu) * T;
     float* const out_v = scores + ((size_t)b * Hq + h0 + hu + 2) * T;
-    // D == 128: the scores of two units (32 rows x 8 heads) gather in a 1 KB stage per
-    // wave (the query operands' LDS, free once they are in registers) and leave as one
-    // store of 16 bytes per lane, a whole 128-byte line per head (lane l: head l / 8,
-    // rows 4 (l % 8) .. + 3)
+    // Batched path: the scores of two row groups (32 rows x 8 heads) gather in a 1 KB
+    // stage per wave (the query operands' LDS, free once they are in registers) and leave
+    // as one store of 16 bytes per lane, a whole 128-byte line per head (lane l: head
+    // l / 8, rows 4 (l % 8) .. + 3)
     float *stg = (float *)qa + wave * (kQkHeads * 32);
     const bool rows16 = (T & 3u) == 0u && ((uintptr_t)scores & 15u) == 0u;   // rows 16-byte aligned
     const uint32_t sh = lane >> 3, sr = 4u * (lane & 7u);
     float *const out_s = scores + ((size_t)b * Hq + h0 + sh) * T;
+    // the source lane of the norm of (row group rg, block j) of a batch, and the score of
+    // a finished row group into the stage
+    auto batch_norm = [&](int rg, int j, uint16_t na, uint16_t nb) -> float {
+        const int src = (16 * rg + (int)n) * (int)MD + j;
+        const uint16_t nr16 = (uint16_t)__shfl((int)(uint32_t)(16 * rg * (int)MD < 64 ? na : nb),
+                                              src & 63, 64);
+        return (float)__builtin_bit_cast(_Float16, nr16);
+    };
 
     f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t k0 = 0;
-    if constexpr (ONE_BLOCK) {
-        // Whole batches (128 rows inside the wave's range, 16-byte aligned score
+    if constexpr (FAST) {
+        // Whole batches (128 / MF rows inside the wave's range, 16-byte aligned score
         // rows): the next batch's loads are unconditional (rows clamped inside the
-        // chunk), every lane stores a 16-byte score line per unit pair (a lane whose
-        // head is past the pass's last one writes that head's line again, with the
+        // chunk), every lane stores a 16-byte score line per pair of row groups (a lane
+        // whose head is past the pass's last one writes that head's line again, with the
         // same values), and the next batch's codes are taken at the end of the batch.
-        // The loop body then has no branch around a memory operation, and the wait
-        // for the prefetched codes counts exactly the score stores issued after them.
-        const uint32_t nfull = rows16 && first < last ? (last - first) / 128u * kQkDepth : 0u;
+        // The loop body then has no branch around a memory operation, and the wait for
+        // the prefetched codes counts exactly the score stores issued after them.
+        constexpr uint32_t RPB = 16 * kQkDepth / MD;   // rows per batch
+        const uint32_t nfull = rows16 && first < last ? (last - first) / RPB * kQkDepth : 0u;
         const uint32_t shf = min(sh, nh - 1u);
         float *const out_f = scores + ((size_t)b * Hq + h0 + shf) * T;
         uint32_t wc[kQkDepth][LW];
@@ -1097,20 +1117,21 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             fetch_norms(k0 + kQkDepth, nna, nnb);
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d) {
-                const uint16_t nr16 = (uint16_t)__shfl((int)(uint32_t)(d < 4 ? nca : ncb),
-                                                       16 * (d & 3) + (int)n, 64);
-                const f4_t Du = qk_unit<BITS>(A, wc[d], tcopy) *
-                                (float)__builtin_bit_cast(_Float16, nr16);
-                float s0 = Du[0], s1 = Du[1], s2 = Du[2], s3 = Du[3];
-                swap32(s0, s1);
-                swap32(s2, s3);
-                stg[hu * 32 + 16 * (d & 1) + n] = (s0 + s1) * pw_u;
-                stg[(hu + 2) * 32 + 16 * (d & 1) + n] = (s2 + s3) * pw_v;
-                if (d & 1) {
-                    wave_lds_sync();
-                    const float4 sv = *(const float4 *)(stg + shf * 32 + sr);
-                    *(float4 *)(out_f + first + (k0 + d - 1u) * 16u + sr) = sv;
-                    wave_lds_sync();   // the stage is read before the next pair writes it
+                const int rg = d / (int)MD, jb = d % (int)MD;   // row group, block
+                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca, ncb);
+                acc = jb == 0 ? Du : acc + Du;
+                if (jb == (int)MD - 1) {
+                    float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
+                    swap32(s0, s1);
+                    swap32(s2, s3);
+                    stg[hu * 32 + 16 * (rg & 1) + n] = (s0 + s1) * pw_u;
+                    stg[(hu + 2) * 32 + 16 * (rg & 1) + n] = (s2 + s3) * pw_v;
+                    if (rg & 1) {
+                        wave_lds_sync();
+                        const float4 sv = *(const float4 *)(stg + shf * 32 + sr);
+                        *(float4 *)(out_f + first + (k0 / MD + rg - 1u) * 16u + sr) = sv;
+                        wave_lds_sync();   // the stage is read before the next pair writes it
+                    }
                 }
             }
 #pragma unroll
@@ -1122,8 +1143,8 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
             ncb = nnb;
         }
     }
-    // Remaining units (all of them for D = 256; at most one ragged batch for D = 128,
-    // whose codes are already in wn).
+    // Remaining units (all of them on the general path; at most one ragged batch on the
+    // batched path, whose codes are already in wn).
     for (; k0 < nunits; k0 += kQkDepth) {
         uint32_t wc[kQkDepth][LW];
         uint16_t nc[kQkDepth];
@@ -1139,36 +1160,25 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
                 fetch(k0 + kQkDepth + d, wn[d], nn[d]);
-            if constexpr (ONE_BLOCK)
+            if constexpr (FAST)
                 fetch_norms(k0 + kQkDepth, nna, nnb);
         }
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
             const uint32_t k = k0 + d;
-            const uint32_t gi = ONE_BLOCK ? k : k / m;
-            const uint32_t j = ONE_BLOCK ? 0u : k - gi * m;
-            if constexpr (!ONE_BLOCK)
-                load_a(j, A);
-            const uint32_t *w = wc[d];
-            uint16_t nr16 = nc[d];
-            if constexpr (ONE_BLOCK)
-                nr16 = (uint16_t)__shfl((int)(uint32_t)(d < 4 ? nca : ncb), 16 * (d & 3) + (int)n, 64);
-            const float nf = (float)__builtin_bit_cast(_Float16, nr16);
-            const f4_t Du = qk_unit<BITS>(A, w, tcopy);
-            if constexpr (ONE_BLOCK)
-                acc = Du * nf;
-            else
-                acc += Du * nf;
-            if (ONE_BLOCK || j == m - 1u) {
-                // rows h (hi) and 8 + h (lo) sit in lanes l and l + 32: one swap pairs them
-                float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
-                swap32(s0, s1);
-                swap32(s2, s3);
-                const float u = (s0 + s1) * pw_u, v = (s2 + s3) * pw_v;
-                if constexpr (ONE_BLOCK) {
-                    stg[hu * 32 + 16 * (d & 1) + n] = u;
-                    stg[(hu + 2) * 32 + 16 * (d & 1) + n] = v;
-                    if (d & 1) {
+            if constexpr (FAST) {
+                const int rg = d / (int)MD, jb = d % (int)MD;
+                const uint32_t gi = k / MD;
+                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca, ncb);
+                acc = jb == 0 ? Du : acc + Du;
+                if (jb == (int)MD - 1) {
+                    // rows h (hi) and 8 + h (lo) sit in lanes l and l + 32: one swap pairs them
+                    float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
+                    swap32(s0, s1);
+                    swap32(s2, s3);
+                    stg[hu * 32 + 16 * (rg & 1) + n] = (s0 + s1) * pw_u;
+                    stg[(hu + 2) * 32 + 16 * (rg & 1) + n] = (s2 + s3) * pw_v;
+                    if (rg & 1) {
                         wave_lds_sync();
                         const float4 sv = *(const float4 *)(stg + sh * 32 + sr);
                         const uint32_t t = first + (gi - 1u) * 16u + sr;   // the pair's first row + sr
@@ -1185,7 +1195,18 @@ __global__ __launch_bounds__(256, kQkGroupsPerCu) void qk_kernel(const uint8_t *
                         }
                         wave_lds_sync();   // the stage is read before the next pair writes it
                     }
-                } else {
+                }
+            } else {
+                const uint32_t gi = k / m;
+                const uint32_t j = k - gi * m;
+                load_a(j, A[0]);
+                const float nf = (float)__builtin_bit_cast(_Float16, nc[d]);
+                acc += qk_unit<BITS>(A[0], wc[d], tcopy) * nf;
+                if (j == m - 1u) {
+                    float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
+                    swap32(s0, s1);
+                    swap32(s2, s3);
+                    const float u = (s0 + s1) * pw_u, v = (s2 + s3) * pw_v;
                     const uint32_t t = first + gi * 16u + n;
                     if (t < last) {
                         if (hu < nh)
@@ -1941,7 +1962,7 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
     // batches of kQkDepth units per wave, at most 65535 row chunks.
     const int64_t step = (int64_t)kWavesPerGroup * 16 * (m >= kQkDepth ? 1 : kQkDepth / m);
     const int64_t pairs = B * Hkv * passes;
-    const int64_t round = (int64_t)cu_count() * kQkGroupsPerCu;
+    const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(m);
     int64_t tpg = (T * pairs + round - 1) / round;
     tpg = tpg < (T + 65534) / 65535 ? (T + 65534) / 65535 : tpg;
     tpg = ((tpg + step - 1) / step) * step;
@@ -1968,8 +1989,8 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
         return (int)hipGetLastError();
     };
     if (bits == 3)
-        return m == 1 ? launch(qk_kernel<3, true>) : launch(qk_kernel<3, false>);
-    return m == 1 ? launch(qk_kernel<2, true>) : launch(qk_kernel<2, false>);
+        return m == 1 ? launch(qk_kernel<3, 1>) : m == 2 ? launch(qk_kernel<3, 2>) : launch(qk_kernel<3, 0>);
+    return m == 1 ? launch(qk_kernel<2, 1>) : m == 2 ? launch(qk_kernel<2, 2>) : launch(qk_kernel<2, 0>);
 }
 
 

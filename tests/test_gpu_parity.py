@@ -187,6 +187,10 @@ def _qk_case(bits, B, Hkv, G, Tc, T, D, seed, q_mul=None, scale=None):
     (1, 2, 4, 5000, 5000, 128),  # score rows 16-byte aligned: whole 128-row batches, then a ragged one
     (1, 1, 12, 1000, 1000, 128), # whole batches in passes of eight and four heads
     (2, 2, 4, 700, 644, 128),    # whole batches with Tc > T, waves past the last row
+    (1, 2, 4, 5000, 5000, 256),  # head_dim 256: whole 64-row batches, then a ragged one
+    (1, 2, 4, 5000, 4999, 256),  # head_dim 256, ragged last group
+    (1, 1, 12, 1000, 1000, 256), # head_dim 256, passes of eight and four heads
+    (2, 2, 4, 700, 644, 256),    # head_dim 256, Tc > T, waves past the last row
 ])
 def test_qk_scores(bits, case):
     B, Hkv, G, Tc, T, D = case

@@ -175,6 +175,46 @@ def test_head_dim_256_turbo2_distortion(head_dim_256):
     assert 0.05 < mse < 0.13
 
 
+def test_head_dim_256_read_path_every_element(head_dim_256):
+    """The fused read over the same head_dim-256 cache, as bench.py times it: its 32 K
+    layers as a batch of 32 sequences (4 kv heads, 16 query heads, GQA 4, all 32768
+    rows): every one of the 16.8M q.K scores and every output of the fused attention
+    over the K and V layers against the oracle over the same GPU-written caches."""
+    c = head_dim_256
+    w, bits = c["w"], c["bits"]
+    B, Hkv, T, D, G = w.L, w.H, w.T, w.D, 4
+    Hq = Hkv * G
+    kc, kn = c["codes"][: w.L], c["norms"][: w.L]
+    vc, vn = c["codes"][w.L:], c["norms"][w.L:]
+    q = gen.queries(w.seed, B, Hq, D, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=DEV)
+    tq.tq_qk_scores(bits, kc, kn, q, scale, scores)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    tq.tq_attn_decode(bits, kc, kn, vc, vn, q, scale, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(scores).all()) and bool(torch.isfinite(out).all())
+    kcn, knn, qn = kc.cpu().numpy(), kn.cpu().numpy(), q.cpu().numpy()
+    ref = oracle.qk_scores(bits, kcn, knn, qn, scale)
+    # ||k_hat|| per row over both blocks, from the oracle's decode, one layer at a time
+    knorm = np.empty((B, Hkv, T))
+    for l in range(B):
+        xh, _ = oracle.decode_blocks(bits, kcn[l].reshape(-1, 16 * bits), knn[l].reshape(-1))
+        knorm[l] = np.sqrt((xh.reshape(Hkv, T, -1) ** 2).sum(axis=-1))
+        del xh
+    qnorm = scale * np.linalg.norm(qn.astype(np.float64), axis=2)[:, :, None]
+    print(check_scores_torch(scores, ref, qnorm, np.repeat(knorm, G, axis=1), "head_dim 256 q.K"))
+    del ref, knorm
+    vcn, vnn = vc.cpu().numpy(), vn.cpu().numpy()
+    aref = oracle.attn_decode(bits, kcn, knn, vcn, vnn, qn, scale)
+    vmax = np.empty((B, Hkv))
+    for l in range(B):
+        xh, _ = oracle.decode_blocks(bits, vcn[l].reshape(-1, 16 * bits), vnn[l].reshape(-1))
+        vmax[l] = np.abs(xh.reshape(Hkv, -1)).max(axis=1)
+        del xh
+    print(check_attn(out.cpu().numpy(), aref, np.repeat(vmax, G, axis=1), T, "head_dim 256 attention"))
+
+
 # ---------------------------------------------------------------- decode step
 
 @pytest.fixture(scope="module")

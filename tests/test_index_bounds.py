@@ -49,6 +49,8 @@ def test_constants_match_the_kernels():
     assert "constexpr int attn_depth(int M) { return 4 / M; }" in src
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
     assert "if (tpg > 8192)" in src and "65535" in src
+    assert "constexpr int qk_groups_per_cu(int64_t m) { return m == 2 ? 3 : kQkGroupsPerCu; }" in src
+    assert "const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(m);" in src
 
 
 def cdiv(a, b):
@@ -89,7 +91,7 @@ def qk_grid(B, Hkv, T, m, Hq, cu):
     passes = cdiv(G, QK_HEADS)
     step = WAVES * 16 * (1 if m >= QK_DEPTH else QK_DEPTH // m)
     pairs = B * Hkv * passes
-    rnd = cu * QK_GROUPS_PER_CU
+    rnd = cu * (3 if m == 2 else QK_GROUPS_PER_CU)
     tpg = cdiv(T * pairs, rnd)
     tpg = max(tpg, cdiv(T, 65535))
     tpg = max(rup(tpg, step), step)
@@ -124,7 +126,8 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
     Hq, m, CB = Hkv * G, D // 128, 16 * bits
     G_, passes, pairs, chunks, tpg = qk_grid(B, Hkv, T, m, Hq, cu)
     assert tpg % (WAVES * 16) == 0
-    one = m == 1
+    fast = m <= 2             # the batched path (one or two blocks per row)
+    MD = m if fast else 1
     codes = Buf("k_codes", B * Hkv * Tc * m * CB)
     norms = Buf("k_norms", B * Hkv * Tc * m)
     q = Buf("q", B * Hq * D)
@@ -138,7 +141,7 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
     # query loads: the two preloaded head slots (D == 128), or every slice of every head
     for s in range(2):
         hh = wave + WAVES * s
-        if one:
+        if m == 1:
             head = h0 + np.where(hh < nh, hh, 0)
             q.check((b * Hq + head) * 128 + LANE)
             q.check((b * Hq + head) * 128 + 64 + LANE)
@@ -149,43 +152,56 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
                 q.check(base + 64 + LANE, mask=hh < nh)
     # code loads of every unit the loops may request (a superset: the loads clamp)
     for k in range(kmax):
-        gi, j = (k, 0) if one else (k // m, k % m)
+        gi, j = k // m, k % m
         tb = np.minimum(first + gi * 16, t_end - 1)
         r = np.minimum(N16, t_end - 1 - tb)
         blk0 = (row0 + tb) * m + j
         byte = blk0 * CB + r * m * CB + PART * 4 * bits
         codes.check(byte, width=4 * bits, align=4)
-        if not one:
+        if not fast:
             norms.check(blk0 + r * m)
-    if one:   # a batch's norms: two loads per lane
+    if fast:   # a batch's norms: two loads per lane, clamped to the chunk's last element
+        emax = (row0 + t_end - 1) * MD + (MD - 1)
         for k in range(0, kmax, QK_DEPTH):
-            norms.check(row0 + np.minimum(first + 16 * k + LANE, t_end - 1))
-            norms.check(row0 + np.minimum(first + 16 * k + 64 + LANE, t_end - 1))
+            e0 = (row0 + first + 16 * (k // MD)) * MD
+            norms.check(np.minimum(e0 + LANE, emax))
+            norms.check(np.minimum(e0 + 64 + LANE, emax))
+            assert np.all(emax < B * Hkv * Tc * m)
     # score stores
-    if one:
+    if fast:
         rows16 = T % 4 == 0          # the tests' score buffers are 16-byte aligned
         sh, sr = LANE >> 3, 4 * (LANE & 7)
-        nfull = np.where(rows16 & (first < last), (last - first) // 128 * QK_DEPTH, 0)
+        rpb = 16 * QK_DEPTH // MD    # rows per batch
+        nfull = np.where(rows16 & (first < last), (last - first) // rpb * QK_DEPTH, 0)
         shf = np.minimum(sh, nh - 1)
-        # whole batches: every lane stores a 16-byte score line per pair of units
+        # whole batches: a 16-byte score line per lane per pair of row groups
         for k0 in range(0, int(nfull.max()) if nfull.size else 0, QK_DEPTH):
             live = k0 < nfull
-            for d in range(1, QK_DEPTH, 2):
-                row = first + (k0 + d - 1) * 16 + sr
+            for rg in range(1, QK_DEPTH // MD, 2):
+                row = first + (k0 // MD + rg - 1) * 16 + sr
                 assert np.all((row + 3 < last)[np.broadcast_to(live, row.shape)])
                 scores.check((b * Hq + h0 + shf) * T + row, width=4, mask=live, align=4)
         # the ragged batch: the general loop, from nfull to the end of the units
         for k in range(0, kmax - QK_DEPTH):
-            live = (k >= nfull) & (k < rup_arr(nunits, QK_DEPTH)) & (k % 2 == 1)
+            d = k % QK_DEPTH
+            rg, jb = d // MD, d % MD
+            if jb != MD - 1 or rg % 2 == 0:
+                continue
+            live = (k >= nfull) & (k < rup_arr(nunits, QK_DEPTH))
             if not live.any():
                 continue
-            t = first + (k - 1) * 16 + sr
+            t = first + (k // MD - 1) * 16 + sr
             ok = live & (sh < nh)
             vec = ok & rows16 & (t + 3 < last)
             scores.check((b * Hq + h0 + sh) * T + t, width=4, mask=vec, align=4)
             for i in range(4):
                 el = ok & ~vec & (t + i < last)
                 scores.check((b * Hq + h0 + sh) * T + t + i, mask=el)
+        # LDS: the score stage (1 KB per wave)
+        hu = 4 * (PART & 1) + (LANE >> 5)
+        for rgp in range(2):
+            assert ((hu + 2) * 32 + 16 * rgp + N16).max() < 256
+        assert shf.max() * 32 + 4 * 7 + 3 < 256
     else:
         hu = 4 * (PART & 1) + (LANE >> 5)
         for k in range(int(nunits.max()) if nunits.size else 0):
@@ -194,12 +210,6 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
             ok = live & (t < last)
             scores.check((b * Hq + h0 + hu) * T + t, mask=ok & (hu < nh))
             scores.check((b * Hq + h0 + hu + 2) * T + t, mask=ok & (hu + 2 < nh))
-    # LDS: the score stage (1 KB per wave) and the query operands of all m blocks
-    if one:
-        hu = 4 * (PART & 1) + (LANE >> 5)
-        for d in range(2):
-            assert ((hu + 2) * 32 + 16 * d + N16).max() < 256
-        assert shf.max() * 32 + 4 * 7 + 3 < 256
     return codes.n + norms.n + q.n + scores.n
 
 
