@@ -1265,9 +1265,12 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
 // larger E rescales acc by a power of two, the way a larger score rescales it by
 // exp(m_old - m_new).
 
-// Workgroups per CU: LDS (41 / 45 KB turbo3, 62 / 66 KB turbo2 for head_dim 128 / 256)
-// and VGPRs allow three turbo3 groups, two turbo2; also the target of the row chunking.
-constexpr int attn_groups_per_cu(int bits) { return bits == 3 ? 3 : 2; }
+// Workgroups per CU, also the target of the row chunking.  turbo2's LDS (62 / 66 KB for
+// head_dim 128 / 256) allows two.  turbo3 (41 / 45 KB) runs three for head_dim 128 and
+// two for 256, whose second block's query operands (32 VGPRs) and accumulators do not
+// fit three groups' registers; reading the operands from LDS at each use instead costs
+// more than the third group gains (325 against 248 us at 16 x 8 x 32768 rows).
+constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 3 : 2; }
 // M = blocks per row (head_dim 128 M).  A batch is 64 / M rows (4 / M 16-row units), so
 // that one norm load per lane covers its 64 (row, block) norms and the units in flight
 // hold the same bytes for both head dims.
@@ -1288,7 +1291,7 @@ constexpr int attn_vtable_bytes(int bits) { return bits == 3 ? 0 : 16 * kLdsCopi
 // M: 128-blocks per row (1 or 2); each row's score sums its blocks' dot products, each
 // block has its own value norms, weights and P.V accumulators.
 template <int BITS, int NHS, int M>
-__global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_kernel(
+__global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial_kernel(
     const uint8_t *__restrict__ k_codes, const uint16_t *__restrict__ k_norms,
     const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
     const uint16_t *__restrict__ q, float *__restrict__ work, uint32_t Hkv, int64_t Tc,
@@ -1395,8 +1398,8 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
     qk_prepare_queries<M == 1>(qa, pw_s, q, b, Hq, h0, nh, (uint32_t)M, wave, lane, scale, sg, qpre);
     __syncthreads();
 
-    // query operands of block jb for this lane's row (lane % 16) and value run; one
-    // block: kept in registers, two: read from LDS where they are used
+    // query operands of block jb for this lane's row (lane % 16) and value run, kept in
+    // registers
     auto load_a = [&](uint32_t jb, h8_t (&Aj)[8]) {
         const _Float16 *arow = qa + jb * 2048 + n * kBlock + part * 32;
 #pragma unroll
@@ -1406,9 +1409,10 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
             Aj[c] = __builtin_bit_cast(h8_t, u4_t{x01, x01, x23, x23});
         }
     };
-    h8_t A[8];
-    if constexpr (M == 1)
-        load_a(0, A);
+    h8_t A[M][8];
+#pragma unroll
+    for (int jb = 0; jb < M; ++jb)
+        load_a(jb, A[jb]);
     const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)ktable + (lane % NC) * EB;
     const uint32_t vcopy = (uint32_t)(uintptr_t)(lds_u8 *)vtable + (lane % kLdsCopies8) * 8;
     // after the hi/lo combine, lane l holds heads hu and hu + 2 of token l % 16
@@ -1469,14 +1473,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS)) void attn_partial_ke
                 const int src = (16 * d + (int)n) * M + jb;   // the lane holding this norm
                 const uint16_t nk16 = (uint16_t)__shfl((int)nkc, src, 64);
                 const uint16_t nv16 = (uint16_t)__shfl((int)nvc, src, 64);
-                f4_t Du;
-                if constexpr (M == 1) {
-                    Du = qk_unit<BITS>(A, wk[d][0], tcopy);
-                } else {
-                    h8_t Aj[8];
-                    load_a(jb, Aj);
-                    Du = qk_unit<BITS>(Aj, wk[d][jb], tcopy);
-                }
+                const f4_t Du = qk_unit<BITS>(A[jb], wk[d][jb], tcopy);
                 sc += Du * (float)__builtin_bit_cast(_Float16, nk16);
                 nvd[d][jb] = (float)__builtin_bit_cast(_Float16, nv16);
                 nmax = __builtin_fmaxf(nmax, nvd[d][jb]);
@@ -2031,7 +2028,7 @@ int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq,
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
     const int64_t step = (int64_t)kWavesPerGroup * 16 * attn_depth((int)m);
-    const int64_t round = 256 * attn_groups_per_cu(bits);
+    const int64_t round = 256 * attn_groups_per_cu(bits, (int)m);
     int64_t rows = (T * B * Hkv * passes + round - 1) / round;
     rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
     rows = ((rows + step - 1) / step) * step;

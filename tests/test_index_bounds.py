@@ -30,7 +30,7 @@ WAVES = 4                 # kWavesPerGroup
 QK_DEPTH = 8              # kQkDepth
 QK_HEADS = 8              # kQkHeads
 QK_GROUPS_PER_CU = 4      # kQkGroupsPerCu
-ATTN_GROUPS = {3: 3, 2: 2}   # attn_groups_per_cu(bits)
+ATTN_GROUPS = {(3, 1): 3, (3, 2): 2, (2, 1): 2, (2, 2): 2}   # attn_groups_per_cu(bits, M)
 
 
 def test_constants_match_the_kernels():
@@ -45,7 +45,8 @@ def test_constants_match_the_kernels():
     assert const("kQkDepth") == QK_DEPTH
     assert const("kQkHeads") == QK_HEADS
     assert const("kQkGroupsPerCu") == QK_GROUPS_PER_CU
-    assert "constexpr int attn_groups_per_cu(int bits) { return bits == 3 ? 3 : 2; }" in src
+    assert "constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 3 : 2; }" in src
+    assert "const int64_t round = 256 * attn_groups_per_cu(bits, (int)m);" in src
     assert "constexpr int attn_depth(int M) { return 4 / M; }" in src
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
     assert "if (tpg > 8192)" in src and "65535" in src
@@ -223,7 +224,7 @@ def attn_chunk_rows(bits, B, Hkv, T, Hq, M):
     G = Hq // Hkv
     passes = cdiv(G, QK_HEADS)
     step = WAVES * 16 * (4 // M)
-    rnd = 256 * ATTN_GROUPS[bits]
+    rnd = 256 * ATTN_GROUPS[(bits, M)]
     rows = cdiv(T * B * Hkv * passes, rnd)
     rows = max(rows, cdiv(T, 65535))
     return max(rup(rows, step), step)
