@@ -994,16 +994,18 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
     const uint32_t nunits = ngroups * m;
 
     // Codes (and, on the general path, the norm) of this lane's run of unit k.  Loads
-    // are unconditional (rows past the wave's range read valid rows of the chunk, at
-    // most row t_end - 1, and are never stored), so the prefetch is straight-line code;
-    // the group's base address is wave-uniform (scalar) and each lane adds a 32-bit
-    // offset.
+    // are unconditional, so the prefetch is straight-line code: rows past the wave's
+    // range are clamped to its last row (a wave without rows: the chunk's last), so they
+    // re-read lines the wave has just fetched instead of the next wave's rows, which
+    // would come from HBM a second time; their values are never stored.  The group's
+    // base address is wave-uniform (scalar) and each lane adds a 32-bit offset.
     const uint32_t row_bytes = m * CB;
+    const uint32_t lastc = first < last ? last - 1u : t_end - 1u;
     auto fetch = [&](uint32_t k, uint32_t (&w)[LW], uint16_t &nr) {
         const uint32_t gi = FAST ? k / MD : k / m;
         const uint32_t j = k - gi * m;
-        const uint32_t tb = min(first + gi * 16u, t_end - 1u);
-        const uint32_t r = min(n, t_end - 1u - tb);
+        const uint32_t tb = min(first + gi * 16u, lastc);
+        const uint32_t r = min(n, lastc - tb);
         const size_t blk0 = (row0 + tb) * m + j;
         const uint32_t *src =
             (const uint32_t *)(k_codes + blk0 * CB + (__umul24(r, row_bytes) + part * (4 * BITS)));
@@ -1015,13 +1017,13 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
     };
     // Batched path: a batch of kQkDepth units holds 128 (row, block) pairs, whose norms
     // come in two loads (elements e0 + lane and e0 + 64 + lane from the batch's first
-    // row, clamped to the chunk's last element); each unit takes its pair's norm from
-    // the lane that holds it.  A separate small load per unit would cost the memory
-    // pipeline about as much as the unit's codes.
+    // row, clamped to the last element of the wave's last row, as the codes); each unit
+    // takes its pair's norm from the lane that holds it.  A separate small load per unit
+    // would cost the memory pipeline about as much as the unit's codes.
     static_assert(kQkDepth * 16 == 128, "two norm loads per batch");
     auto fetch_norms = [&](uint32_t k, uint16_t &na, uint16_t &nb) {
         const size_t e0 = (row0 + first + 16u * (k / MD)) * MD;
-        const size_t emax = (row0 + t_end - 1u) * MD + (MD - 1u);
+        const size_t emax = (row0 + lastc) * MD + (MD - 1u);
         na = ld_stream(k_norms + min(e0 + lane, emax));
         nb = ld_stream(k_norms + min(e0 + 64u + lane, emax));
     };

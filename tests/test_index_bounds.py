@@ -51,6 +51,10 @@ def test_constants_match_the_kernels():
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
     assert "if (tpg > 8192)" in src and "65535" in src
     assert "constexpr int qk_groups_per_cu(int64_t m) { return m == 2 ? 3 : kQkGroupsPerCu; }" in src
+    # q.K's prefetch clamp, as replayed below
+    assert "const uint32_t lastc = first < last ? last - 1u : t_end - 1u;" in src
+    assert "const uint32_t tb = min(first + gi * 16u, lastc);" in src
+    assert "const size_t emax = (row0 + lastc) * MD + (MD - 1u);" in src
     assert "const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(m);" in src
 
 
@@ -151,18 +155,22 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
                 base = (b * Hq + h0 + hh) * m * 128 + j * 128
                 q.check(base + LANE, mask=hh < nh)
                 q.check(base + 64 + LANE, mask=hh < nh)
-    # code loads of every unit the loops may request (a superset: the loads clamp)
+    # code loads of every unit the loops may request (a superset: the loads clamp to the
+    # wave's last row, so a wave never reads another wave's rows)
+    lastc = np.where(first < last, last - 1, t_end - 1)
+    own_lo = np.where(first < last, first, 0)
     for k in range(kmax):
         gi, j = k // m, k % m
-        tb = np.minimum(first + gi * 16, t_end - 1)
-        r = np.minimum(N16, t_end - 1 - tb)
+        tb = np.minimum(first + gi * 16, lastc)
+        r = np.minimum(N16, lastc - tb)
+        assert np.all((tb + r <= lastc) & (tb + r >= own_lo)), "a load outside the wave's rows"
         blk0 = (row0 + tb) * m + j
         byte = blk0 * CB + r * m * CB + PART * 4 * bits
         codes.check(byte, width=4 * bits, align=4)
         if not fast:
             norms.check(blk0 + r * m)
-    if fast:   # a batch's norms: two loads per lane, clamped to the chunk's last element
-        emax = (row0 + t_end - 1) * MD + (MD - 1)
+    if fast:   # a batch's norms: two loads per lane, clamped to the wave's last element
+        emax = (row0 + lastc) * MD + (MD - 1)
         for k in range(0, kmax, QK_DEPTH):
             e0 = (row0 + first + 16 * (k // MD)) * MD
             norms.check(np.minimum(e0 + LANE, emax))
