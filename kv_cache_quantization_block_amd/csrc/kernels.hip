@@ -212,6 +212,27 @@ __device__ __forceinline__ void levels_to_lds(float *lv, const Codebook &cb)
     }
 }
 
+// Wave priority by the work a wave has left.  The fused read kernels split their rows
+// statically, one equal share per wave, and the SIMDs' arbiters favour older waves: with
+// every wave at the same priority, waves of equal work finish up to 1.6x apart (at the
+// 16-sequence decode step, q.K's waves took 37-60 us and the attention's 80-123 us), and
+// a launch lasts as long as its slowest wave.  Giving the waves with more work left the
+// higher priority lets the lagging waves issue first and keeps all of them in step
+// (spans 60 -> 56 us and 120 -> 112 us; all waves end within the last eighth of the work).
+// Called once per batch with the batch index and the batch count; wave-uniform.
+__device__ __forceinline__ void prio_by_progress(uint32_t done, uint32_t total)
+{
+    const uint32_t rem = total - done;
+    if (rem * 2u > total)
+        __builtin_amdgcn_s_setprio(3);
+    else if (rem * 4u > total)
+        __builtin_amdgcn_s_setprio(2);
+    else if (rem * 8u > total)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Order LDS traffic between the lanes of one wavefront (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -1113,6 +1134,7 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
             for (int i = 0; i < LW; ++i)
                 wc[d][i] = wn[d][i];
         for (; k0 < nfull; k0 += kQkDepth) {
+            prio_by_progress(k0, nfull);
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
                 fetch(k0 + kQkDepth + d, wn[d], nn[d]);
@@ -1455,6 +1477,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
     // batch's norms are requested first, so that they are the oldest loads in flight
     // when that batch starts
     for (uint32_t k0 = 0; k0 < nunits; k0 += DEPTH) {
+        prio_by_progress(k0, nunits);
         uint32_t nkn, nvn;
         fetch_norms(k0 + DEPTH, nkn, nvn);
         // scores of heads hu, hu + 2 for token n of each unit (as qk_kernel, summed over
