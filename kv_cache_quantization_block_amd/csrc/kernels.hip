@@ -555,6 +555,42 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
     // workgroup (a wave has a single tile, so building them per lane would cost it
     // about a sixth of its VALU work)
     __shared__ u4_t smask_s[ROT ? 16 : 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n = lane & 15u, G = lane >> 4;
+    const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
+    // cache position of block b: b itself when the cache rows hold exactly the
+    // decoded rows (no division)
+    const bool contig = cache_row_blocks == (int64_t)row_blocks && t0_blocks == 0;
+    auto src_of = [&](uint32_t b) -> int64_t {
+        if (contig)
+            return (int64_t)b;
+        return cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
+    };
+    const uint32_t stride = gridDim.x * kWavesPerGroup;
+    uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
+    // loads of tile t: lane (G, n), G < BITS, takes 16-byte chunk G of block 16 c + n
+    // (one instruction covers 16 whole blocks, contiguous when the cache is); lanes
+    // G >= BITS repeat chunk BITS - 1 (same addresses) and lanes past the tile's blocks
+    // read its last block, so every load is unconditional
+    u4_t C[2];
+    uint16_t N16[2];
+    auto load_tile = [&](uint32_t t) {
+        const uint32_t tb0 = t * kEncTileBlocks;
+        const uint32_t tnb = min(nblocks - tb0, (uint32_t)kEncTileBlocks);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int64_t src = src_of(tb0 + min(16u * c + n, tnb - 1u));
+            C[c] = ld_stream((const u4_t *)(codes + src * CB) + min(G, (uint32_t)BITS - 1u));
+            N16[c] = ld_stream(norms + src);
+        }
+    };
+    // turbo3: the first tile's loads go out before the table set-up and its barriers
+    // (3-5 % on whole caches); turbo2, whose table is a quarter the size, measured 1-3 %
+    // slower that way and loads at the top of the loop
+    constexpr bool kEarly = BITS == 3;
+    if (kEarly && tile < ntiles)
+        load_tile(tile);
     levels_to_lds(lv, cb);
     if constexpr (ROT) {
         if (threadIdx.x >= 64u && threadIdx.x < 80u)
@@ -575,20 +611,6 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
         *(uint2 *)(table + i * 8) = ent_s[i / kLdsCopies8];
     __syncthreads();
 
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t n = lane & 15u, G = lane >> 4;
-    const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
-    // cache position of block b: b itself when the cache rows hold exactly the
-    // decoded rows (no division)
-    const bool contig = cache_row_blocks == (int64_t)row_blocks && t0_blocks == 0;
-    auto src_of = [&](uint32_t b) -> int64_t {
-        if (contig)
-            return (int64_t)b;
-        return cache_block(b, row_blocks, cache_row_blocks, t0_blocks);
-    };
-    const uint32_t stride = gridDim.x * kWavesPerGroup;
-    uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
     if (tile >= ntiles)
         return;
 
@@ -621,21 +643,11 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
     // 0 and 3 read their one dword twice, which keeps G = 3, g' = 3 inside the block)
     const uint32_t fdw = (3u * G) >> 2, fsh = 8u * ((3u * G) & 3u), fhi = fsh > 8u ? 1u : 0u;
 
-    for (; tile < ntiles; tile += stride) {
+    for (;;) {
         const uint32_t b0 = tile * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
-        // loads: lane (G, n), G < BITS, takes 16-byte chunk G of block 16 c + n (one
-        // instruction covers 16 whole blocks, contiguous when the cache is); lanes
-        // G >= BITS repeat chunk BITS - 1 (same addresses) and lanes past nb read the
-        // tile's last block, so every load is unconditional
-        u4_t C[2];
-        uint16_t N16[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int64_t src = src_of(b0 + min(16u * c + n, nb - 1u));
-            C[c] = ld_stream((const u4_t *)(codes + src * CB) + min(G, (uint32_t)BITS - 1u));
-            N16[c] = ld_stream(norms + src);
-        }
+        if (!kEarly)
+            load_tile(tile);
         wave_lds_sync();   // the previous tile's stage reads are done
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -719,6 +731,11 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
                     *(u4_t *)(dst + k * 1024) = r;
             }
         }
+        tile += stride;
+        if (tile >= ntiles)
+            break;
+        if (kEarly)
+            load_tile(tile);   // (a capped grid) the next tile's loads
     }
 }
 
