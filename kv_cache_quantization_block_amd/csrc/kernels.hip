@@ -28,9 +28,13 @@
 //  * q.K: q . (H y) = (H q) . y since H is symmetric, so each query slice is rotated
 //    once per workgroup and the keys' levels enter v_mfma_f32_16x16x32_f16 as fp16
 //    hi / lo pairs read from an LDS table; the decoded key is never formed.
-//  * decode attention: the same scores, an online softmax per 64 rows and P.V on the
-//    matrix cores in the rotated domain, one inverse transform per head at the end
-//    of a second (combine) pass over per-chunk partials.
+//  * decode attention: the same scores, an online softmax per batch of 64 / m rows
+//    (m blocks per row) and P.V on the matrix cores in the rotated domain, one
+//    inverse transform per head at the end of a second (combine) pass over per-chunk
+//    partials.
+//  * both fused read kernels give every wave an equal share of rows and raise the
+//    priority of the waves with the most work left, so that the arbiters' preference
+//    for older waves does not leave a tail of late ones.
 //  * interleaved records: LDS-staged 16-byte moves between the planes and the
 //    50 / 34-byte block records.
 //  * the randomised rotation H D flips fp16 sign bits (XOR) where the kernels load
