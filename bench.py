@@ -268,7 +268,8 @@ class Headline:
                  lambda: tq.tq_qk_scores(self.bits, kc, kn, q, scale, scores))):
             us = time_back_to_back(fn, self.stream, reps)
             res[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(gbs(nbytes, us), 1),
-                         "frac_of_hbm_peak": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4)}
+                         "frac_of_hbm_peak": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4),
+                         "kernel_median_us": round(launch_median(tq, fn, reps), 2)}
         del tok, q, scores
         return res
 
@@ -343,6 +344,28 @@ def time_back_to_back(fn, stream, reps):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def launch_median(tq, fn, reps):
+    """Median microseconds of one kernel launch measured by the launch itself (the events
+    recorded from its dispatch packet, tq_time_next_launch), over `reps` launches issued
+    back to back after two untimed: the kernel's own duration, without the host's launch
+    latency.  fn must launch exactly one kernel."""
+    import statistics
+    import torch
+    fn()
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:   # torch creates an event's HIP event at its first record
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        tq.tq_time_next_launch(e0, e1)
+        fn()
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
 
 
 def copy_calibration(dev):
@@ -467,6 +490,9 @@ def decode_step(tq, gen, dev, stream, reps=20):
            "attn_GBps": round(gbs(ab, med["attn"]), 1),
            "attn_frac_of_hbm_peak": round(gbs(ab, med["attn"]) / HBM_PEAK_GBS, 4),
            "append_kv_us": round(med["append_kv"], 2),
+           # the K append's own kernel duration (128 blocks), without host launch latency
+           "append_kernel_us": round(launch_median(
+               tq, lambda: tq.tq_encode(bits, tok["K"], kc, kn, T_ - 1), reps), 2),
            # issue-port utilisation from the committed counters (what binds a kernel
            # that runs below the HBM roofline)
            "qk_issue": issue_utilisation("qk"), "attn_issue": issue_utilisation("attn")}
