@@ -239,6 +239,9 @@ def _attn_case(bits, B, Hkv, G, Tc, T, seed, q_mul=1.0, scale=None, v_mul=1.0, z
     (1, 2, 2, 1, 1),         # one row: the output is that row's value
     (1, 2, 4, 5000, 4999),   # many row chunks and waves, ragged last unit
     (3, 2, 4, 2000, 1500),   # several sequences, T well below Tc
+    (1, 1, 16, 64, 61),      # group 16: two full passes of eight heads
+    (1, 2, 3, 50, 50),       # odd group: one set of four heads, three used
+    (2, 2, 5, 300, 257),     # group 5: two sets in one pass, the second with one head
 ])
 def test_attn_decode(bits, case):
     B, Hkv, G, Tc, T = case
@@ -254,6 +257,9 @@ def test_attn_decode(bits, case):
     (1, 2, 2, 1, 1),         # one row: the output is that row's value
     (1, 2, 4, 5000, 4999),   # many row chunks and waves, ragged last unit
     (3, 2, 4, 2000, 1500),   # several sequences, T well below Tc
+    (1, 1, 16, 64, 61),      # group 16: two full passes of eight heads
+    (1, 2, 3, 50, 50),       # odd group
+    (2, 2, 5, 300, 257),     # group 5: two sets in one pass, the second with one head
 ])
 def test_attn_decode_head_dim_256(bits, case):
     """head_dim 256 (two 128-blocks per row, each with its own norm; section

@@ -344,6 +344,8 @@ ATTN_SHAPES = [
     (1, 2, 2, 1, 1, 128), (1, 2, 4, 5000, 4999, 128), (3, 2, 4, 2000, 1500, 128),
     (1, 2, 4, 100, 97, 256), (2, 1, 8, 40, 33, 256), (1, 1, 12, 300, 300, 256), (1, 3, 1, 70, 70, 256),
     (1, 2, 2, 1, 1, 256), (1, 2, 4, 5000, 4999, 256), (3, 2, 4, 2000, 1500, 256),
+    (1, 1, 16, 64, 61, 128), (1, 2, 3, 50, 50, 128), (2, 2, 5, 300, 257, 128),   # groups 16, 3, 5
+    (1, 1, 16, 64, 61, 256), (1, 2, 3, 50, 50, 256), (2, 2, 5, 300, 257, 256),
     (1, 2, 4, 600, 600, 128), (1, 2, 4, 600, 590, 128), (1, 2, 4, 300, 300, 128),     # extremes
     (1, 2, 4, 600, 600, 256), (1, 2, 4, 600, 590, 256), (1, 2, 4, 300, 300, 256),
     (2, 2, 4, 3000, 3000, 128),                                 # side stream
