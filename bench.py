@@ -248,7 +248,7 @@ class Headline:
         """On the same resident cache: the 1-token append of K and V into row T - 1 of every
         layer (one launch over [96, 8, 1, 128]), and q.K of 32 query heads over the keys of
         all 48 layers (the K half as a batch of 48, one launch: each layer's decode-step
-        scores).  Average of `reps` back-to-back launches after two untimed."""
+        scores).  Average of `reps` back-to-back launches after 0.2 s of untimed ones."""
         import torch
         tq, gen, w = self.tq, self.gen, self.w
         tok = torch.empty((self.Lx, w.H, 1, w.D), dtype=torch.float16, device=self.dev)
@@ -332,12 +332,21 @@ class Headline:
         torch.cuda.empty_cache()
 
 
-def time_back_to_back(fn, stream, reps):
-    """Average microseconds of `reps` back-to-back calls between two events, after two
-    untimed calls (the queue never drains, so host launch latency stays hidden)."""
+def time_back_to_back(fn, stream, reps, settle_s=SETTLE_S):
+    """Average microseconds of `reps` back-to-back calls between two events (the queue
+    never drains, so host launch latency stays hidden), after `settle_s` seconds of the
+    same calls untimed: as for the headline steps, the clocks settle under the call's own
+    sustained load first (launched right after a different kind of load, a kernel's first
+    milliseconds run at the clocks the power manager set for that load)."""
     import torch
-    fn()
-    fn()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_settle >= settle_s:
+            break
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -505,7 +514,7 @@ def decode_step(tq, gen, dev, stream, reps=20):
 def head_dim_256(tq, gen, dev, stream, reps=10):
     """turbo2 encode then decode of a whole head_dim-256 cache (32 layers x 4 kv heads x
     32768 x 256, K and V as one [64, 4, 32768, 256] tensor, 4.3 GB of fp16), average of
-    `reps` back-to-back launches per op after ten untimed ones; then the fused read over
+    `reps` back-to-back launches per op after 0.2 s of untimed ones; then the fused read over
     the same cache: its 32 K layers as a batch of 32 sequences (16 query heads, GQA 4),
     q.K over all 32768 rows and the decode attention over the K and V layers."""
     import torch
@@ -651,7 +660,7 @@ def one_layer(tq, gen, dev, stream, reps=20):
 def copy_bandwidth(dev, stream, nbytes=512 << 20, reps=10):
     """Context for the roofline: what a plain device-to-device copy of 512 MiB (torch's
     copy kernel, read + write counted) reaches on this GPU, HIP events around `reps`
-    back-to-back copies after three untimed ones."""
+    back-to-back copies after 0.2 s of untimed ones."""
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)

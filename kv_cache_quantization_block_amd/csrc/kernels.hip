@@ -795,12 +795,16 @@ inline size_t qk_smem_bytes(int bits, int64_t m)
 
 
 
-// x as packed fp16 (hi, lo): hi = fp16(x), lo = fp16(x - hi) rounded toward zero (hi
-// is exact in fp16, so the truncating pack keeps it).
+// x as packed fp16 (hi, lo): hi = fp16(x), lo = fp16(x - hi), both rounded to nearest
+// even.  Two instructions: the conversion writes hi into the low half, and a mixed-
+// precision FMA takes hi back as an fp16 operand, forms x - hi exactly in fp32 and
+// writes its fp16 rounding into the high half (the compiler's own form takes four).
 __device__ __forceinline__ uint32_t split_pack(float x)
 {
-    const float hi = (float)(_Float16)x;
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi, x - hi));
+    uint32_t d;
+    asm("v_cvt_f16_f32 %0, %1\n\tv_fma_mixhi_f16 %0, -%0, 1.0, %1 op_sel_hi:[1,0,0]"
+        : "=&v"(d) : "v"(x));
+    return d;
 }
 
 
@@ -1310,12 +1314,14 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
 // larger E rescales acc by a power of two, the way a larger score rescales it by
 // exp(m_old - m_new).
 
-// Workgroups per CU, also the target of the row chunking.  turbo2's LDS (62 / 66 KB for
-// head_dim 128 / 256) allows two.  turbo3 (41 / 45 KB) runs three for head_dim 128 and
-// two for 256, whose second block's query operands (32 VGPRs) and accumulators do not
-// fit three groups' registers; reading the operands from LDS at each use instead costs
-// more than the third group gains (325 against 248 us at 16 x 8 x 32768 rows).
-constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 3 : 2; }
+// Workgroups per CU, also the target of the row chunking.  turbo2's LDS (58 KB for
+// either head dim) allows two.  turbo3 (37 KB) runs four for head_dim 128, within 128
+// VGPRs (a few values live only in the prologue and after the loop spill, one reload per
+// batch), and two for 256, whose second block's query operands (32 VGPRs) and
+// accumulators do not fit three groups' registers; reading the operands from LDS at each
+// use instead costs more than the third group gains (325 against 248 us at
+// 16 x 8 x 32768 rows).
+constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 4 : 2; }
 // M = blocks per row (head_dim 128 M).  A batch is 64 / M rows (4 / M 16-row units), so
 // that one norm load per lane covers its 64 (row, block) norms and the units in flight
 // hold the same bytes for both head dims.
@@ -1360,13 +1366,15 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
     static_assert(kMerge <= kTables + kRawBytes + kPtBytes, "the merge reuses the tiles' bytes");
     static_assert(DEPTH * 16 * M == 64, "one norm load per lane per batch");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kTables + kRawBytes + kPtBytes];
-    __shared__ __attribute__((aligned(16))) _Float16 qa[M * 16 * kBlock];
     __shared__ __attribute__((aligned(16))) float ftile[kWavesPerGroup][kQkHeads];
     __shared__ float pw_s[kQkHeads];
     __shared__ float lv[8];
     uint8_t *ktable = smem, *vtable = BITS == 3 ? smem : smem + qk_table_bytes(BITS);
     uint32_t *raw_base = (uint32_t *)(smem + kTables);
     uint32_t *pt_base = (uint32_t *)(smem + kTables + kRawBytes);
+    // the query operands, in the code tiles' bytes until every wave holds them in registers
+    static_assert(M * 16 * kBlock * 2 <= kRawBytes, "qa fits the code tiles");
+    _Float16 *qa = (_Float16 *)raw_base;
 
     const uint32_t pass = blockIdx.x % passes;
     const uint32_t bg = blockIdx.x / passes;           // b * Hkv + g
@@ -1458,6 +1466,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
 #pragma unroll
     for (int jb = 0; jb < M; ++jb)
         load_a(jb, A[jb]);
+    __syncthreads();   // qa's bytes are the code tiles from here on
     const uint32_t tcopy = (uint32_t)(uintptr_t)(lds_u8 *)ktable + (lane % NC) * EB;
     const uint32_t vcopy = (uint32_t)(uintptr_t)(lds_u8 *)vtable + (lane % kLdsCopies8) * 8;
     // after the hi/lo combine, lane l holds heads hu and hu + 2 of token l % 16

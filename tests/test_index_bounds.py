@@ -30,7 +30,7 @@ WAVES = 4                 # kWavesPerGroup
 QK_DEPTH = 8              # kQkDepth
 QK_HEADS = 8              # kQkHeads
 QK_GROUPS_PER_CU = 4      # kQkGroupsPerCu
-ATTN_GROUPS = {(3, 1): 3, (3, 2): 2, (2, 1): 2, (2, 2): 2}   # attn_groups_per_cu(bits, M)
+ATTN_GROUPS = {(3, 1): 4, (3, 2): 2, (2, 1): 2, (2, 2): 2}   # attn_groups_per_cu(bits, M)
 
 
 def test_constants_match_the_kernels():
@@ -45,7 +45,7 @@ def test_constants_match_the_kernels():
     assert const("kQkDepth") == QK_DEPTH
     assert const("kQkHeads") == QK_HEADS
     assert const("kQkGroupsPerCu") == QK_GROUPS_PER_CU
-    assert "constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 3 : 2; }" in src
+    assert "constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 4 : 2; }" in src
     assert "const int64_t round = 256 * attn_groups_per_cu(bits, (int)m);" in src
     assert "constexpr int attn_depth(int M) { return 4 / M; }" in src
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
