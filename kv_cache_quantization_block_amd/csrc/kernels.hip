@@ -1300,7 +1300,7 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
 // product block c is pair 4 n + c: the lane of column n needs positions 8 n .. 8 n + 7
 // of its four tokens, eight codes that are one contiguous 24-bit (turbo3) / 16-bit
 // (turbo2) field of each token's packed block.  Each wave parks its 16 tokens'
-// packed codes in a small LDS tile (a 48-byte row per token) and every lane reads
+// packed codes in a small LDS tile (a 16 BITS-byte row per token and block) and every lane reads
 // its four fields from it and looks the code pairs up: 16 lookups and 8 products per
 // unit for up to four heads, 16 products for eight.
 // The weights are written to a small LDS tile, as packed (hi, lo) fp16 pairs, by the
@@ -1314,14 +1314,18 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
 // larger E rescales acc by a power of two, the way a larger score rescales it by
 // exp(m_old - m_new).
 
-// Workgroups per CU, also the target of the row chunking.  turbo2's LDS (58 KB for
-// either head dim) allows two.  turbo3 (37 KB) runs four for head_dim 128, within 128
-// VGPRs (a few values live only in the prologue and after the loop spill, one reload per
-// batch), and two for 256, whose second block's query operands (32 VGPRs) and
-// accumulators do not fit three groups' registers; reading the operands from LDS at each
-// use instead costs more than the third group gains (325 against 248 us at
-// 16 x 8 x 32768 rows).
-constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 4 : 2; }
+// Workgroups per CU, also the target of the row chunking; NHS = sets of four query heads.
+// head_dim 128: turbo3 (37 KB of LDS) runs four with one head set, within 128 VGPRs (a
+// few values live only in the prologue and after the loop spill, one reload per batch),
+// and three with two sets (153 VGPRs; at four they spill 22); turbo2 (53 KB) runs three.
+// head_dim 256 runs two: the second block's query operands (32 VGPRs) and accumulators do
+// not fit three groups' registers for turbo3, reading the operands from LDS at each use
+// instead costs more than the third group gains (325 against 248 us at 16 x 8 x 32768
+// rows), and turbo2's third group (168 VGPRs) measured no faster.
+constexpr int attn_groups_per_cu(int bits, int NHS, int M)
+{
+    return M == 2 ? 2 : bits == 3 && NHS == 1 ? 4 : 3;
+}
 // M = blocks per row (head_dim 128 M).  A batch is 64 / M rows (4 / M 16-row units), so
 // that one norm load per lane covers its 64 (row, block) norms and the units in flight
 // hold the same bytes for both head dims.
@@ -1342,7 +1346,7 @@ constexpr int attn_vtable_bytes(int bits) { return bits == 3 ? 0 : 16 * kLdsCopi
 // M: 128-blocks per row (1 or 2); each row's score sums its blocks' dot products, each
 // block has its own value norms, weights and P.V accumulators.
 template <int BITS, int NHS, int M>
-__global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial_kernel(
+__global__ __launch_bounds__(256, attn_groups_per_cu(BITS, NHS, M)) void attn_partial_kernel(
     const uint8_t *__restrict__ k_codes, const uint16_t *__restrict__ k_norms,
     const uint8_t *__restrict__ v_codes, const uint16_t *__restrict__ v_norms,
     const uint16_t *__restrict__ q, float *__restrict__ work, uint32_t Hkv, int64_t Tc,
@@ -1354,7 +1358,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
     constexpr int LW = BITS;             // code words per lane and block (32 codes)
     constexpr int DEPTH = attn_depth(M); // units per batch
     constexpr int REC = attn_rec(M);
-    constexpr int RW = 12 * M;           // words per token row of a code tile (48 B per block)
+    constexpr int RW = 4 * BITS * M;     // words per token row of a code tile (16 BITS B per block)
     // LDS: the tables; per unit in flight the packed value codes of its 16 rows (one
     // spare dword read past the last field) and, per block, the weights [head][row] as
     // (hi, lo); after the last unit the same bytes hold the four waves' states
@@ -1524,7 +1528,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
             for (int jb = 0; jb < M; ++jb) {
 #pragma unroll
                 for (int i = 0; i < LW; ++i)
-                    rt[n * RW + 12 * jb + part * LW + i] = wv[d][jb][i];
+                    rt[n * RW + 4 * BITS * jb + part * LW + i] = wv[d][jb][i];
                 const int src = (16 * d + (int)n) * M + jb;   // the lane holding this norm
                 const uint16_t nk16 = (uint16_t)__shfl((int)nkc, src, 64);
                 const uint16_t nv16 = (uint16_t)__shfl((int)nvc, src, 64);
@@ -1602,7 +1606,7 @@ __global__ __launch_bounds__(256, attn_groups_per_cu(BITS, M)) void attn_partial
                     uint64_t ent[2][4];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const uint32_t *row = rt + (8 * kb + 2 * part + j) * RW + 12 * jb + dA;
+                        const uint32_t *row = rt + (8 * kb + 2 * part + j) * RW + 4 * BITS * jb + dA;
                         const uint32_t f = __builtin_amdgcn_alignbit(row[1], row[0], fsh);
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
@@ -2083,7 +2087,7 @@ int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq,
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
     const int64_t step = (int64_t)kWavesPerGroup * 16 * attn_depth((int)m);
-    const int64_t round = 256 * attn_groups_per_cu(bits, (int)m);
+    const int64_t round = 256 * attn_groups_per_cu(bits, G > kQkHeads / 2 ? 2 : 1, (int)m);
     int64_t rows = (T * B * Hkv * passes + round - 1) / round;
     rows = rows < (T + 65534) / 65535 ? (T + 65534) / 65535 : rows;
     rows = ((rows + step - 1) / step) * step;

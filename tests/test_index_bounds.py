@@ -30,7 +30,9 @@ WAVES = 4                 # kWavesPerGroup
 QK_DEPTH = 8              # kQkDepth
 QK_HEADS = 8              # kQkHeads
 QK_GROUPS_PER_CU = 4      # kQkGroupsPerCu
-ATTN_GROUPS = {(3, 1): 4, (3, 2): 2, (2, 1): 2, (2, 2): 2}   # attn_groups_per_cu(bits, M)
+# attn_groups_per_cu(bits, NHS, M), NHS = sets of four query heads (2 when G > 4)
+ATTN_GROUPS = {(3, 1, 1): 4, (3, 2, 1): 3, (2, 1, 1): 3, (2, 2, 1): 3,
+               (3, 1, 2): 2, (3, 2, 2): 2, (2, 1, 2): 2, (2, 2, 2): 2}
 
 
 def test_constants_match_the_kernels():
@@ -45,8 +47,9 @@ def test_constants_match_the_kernels():
     assert const("kQkDepth") == QK_DEPTH
     assert const("kQkHeads") == QK_HEADS
     assert const("kQkGroupsPerCu") == QK_GROUPS_PER_CU
-    assert "constexpr int attn_groups_per_cu(int bits, int M) { return bits == 3 && M == 1 ? 4 : 2; }" in src
-    assert "const int64_t round = 256 * attn_groups_per_cu(bits, (int)m);" in src
+    assert "return M == 2 ? 2 : bits == 3 && NHS == 1 ? 4 : 3;" in src
+    assert "const int64_t round = 256 * attn_groups_per_cu(bits, G > kQkHeads / 2 ? 2 : 1, (int)m);" in src
+    assert "constexpr int RW = 4 * BITS * M;" in src
     assert "constexpr int attn_depth(int M) { return 4 / M; }" in src
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
     assert "if (tpg > 8192)" in src and "65535" in src
@@ -232,7 +235,7 @@ def attn_chunk_rows(bits, B, Hkv, T, Hq, M):
     G = Hq // Hkv
     passes = cdiv(G, QK_HEADS)
     step = WAVES * 16 * (4 // M)
-    rnd = 256 * ATTN_GROUPS[(bits, M)]
+    rnd = 256 * ATTN_GROUPS[(bits, 2 if G > QK_HEADS // 2 else 1, M)]
     rows = cdiv(T * B * Hkv * passes, rnd)
     rows = max(rows, cdiv(T, 65535))
     return max(rup(rows, step), step)
@@ -240,7 +243,7 @@ def attn_chunk_rows(bits, B, Hkv, T, Hq, M):
 
 def replay_attn(bits, B, Hkv, G, Tc, T, D):
     Hq, M, CB = Hkv * G, D // 128, 16 * bits
-    DEPTH, REC, RW = 4 // M, 4 + 128 * M, 12 * M
+    DEPTH, REC, RW = 4 // M, 4 + 128 * M, 4 * bits * M
     passes = cdiv(G, QK_HEADS)
     rows = attn_chunk_rows(bits, B, Hkv, T, Hq, M)
     chunks = cdiv(T, rows)
@@ -288,8 +291,8 @@ def replay_attn(bits, B, Hkv, G, Tc, T, D):
             row = (8 * kb + 2 * PART + j) * RW
             for jb in range(M):
                 dA = (8 * bits * N16) >> 5
-                assert (row + 12 * jb + dA + 1).max() < raw_words
-    assert (N16 * RW + 12 * (M - 1) + PART * bits + bits - 1).max() < raw_words
+                assert (row + 4 * bits * jb + dA + 1).max() < raw_words
+    assert (N16 * RW + 4 * bits * (M - 1) + PART * bits + bits - 1).max() < raw_words
     # the workspace records: thread t -> head t / 32, values 4 (t % 32) .. + 3
     tid = np.arange(256)
     h, v0 = tid >> 5, 4 * (tid & 31)
