@@ -211,7 +211,7 @@ int tq_attn_decode_rot(int type, const uint32_t *signs, const void *k_codes,
  * and statuses; in addition TQ_ERR_WORKSPACE when the sizes need more than
  * TQ_ATTN_SCRATCH_BYTES (tq_attn_workspace_bytes(...) > TQ_ATTN_SCRATCH_BYTES: about
  * 15,000 (sequence, query head, row chunk) partials; the decode step of 16 sequences x
- * 32 heads at 32768 rows needs 1.6 MB), and TQ_ERR_DEVICE when the array's address
+ * 32 heads at 32768 rows needs 2.2 MB), and TQ_ERR_DEVICE when the array's address
  * cannot be found.  No hipMalloc, hipFree or memset.  Every call on a device uses that
  * device's one array: calls that overlap on the same device (other streams, other
  * threads) race on it and must be serialised by the caller.  The array needs no initial
