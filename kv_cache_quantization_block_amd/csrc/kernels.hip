@@ -2081,8 +2081,9 @@ int launch_unpack_records(int bits, const void *records, int64_t nblocks, void *
 }
 
 // Decode attention chunking, from the sizes alone (tq_attn_workspace_bytes needs no
-// device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X, whole batches
-// of attn_depth(m) units per wave, at most 65535 chunks.
+// device): about attn_groups_per_cu workgroups per CU of a 256-CU MI355X (two head sets
+// when G > 4, as the launch picks its kernel), whole batches of attn_depth(m) units per
+// wave, at most 65535 chunks.
 int64_t attn_chunk_rows(int bits, int64_t B, int64_t Hkv, int64_t T, int64_t Hq, int64_t m)
 {
     const int64_t G = Hq / Hkv, passes = (G + kQkHeads - 1) / kQkHeads;
