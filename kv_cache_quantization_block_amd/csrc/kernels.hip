@@ -777,11 +777,16 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const uint8_t *__restric
 
 // (group, block) units whose codes are in flight while the previous ones are
 // scored; a group is the 16 tokens one wave scores at once.
-constexpr int kQkDepth = 8;
+constexpr int kQkDepth = 4;
 constexpr int kQkHeads = 8;         // query heads per pass
 constexpr int kQkGroupsPerCu = 4;   // workgroups per CU the grid aims at (4 waves per SIMD)
-// with two blocks per row the query operands of both stay in registers: 3 groups per CU
-constexpr int qk_groups_per_cu(int64_t m) { return m == 2 ? 3 : kQkGroupsPerCu; }
+// turbo3 with one block per row fits a fifth group (92 VGPRs, 20 KB of LDS); turbo2's
+// 36 KB of LDS allows four; with two blocks per row the query operands of both stay in
+// registers: 3 groups per CU
+constexpr int qk_groups_per_cu(int bits, int64_t m)
+{
+    return m == 2 ? 3 : bits == 3 && m == 1 ? 5 : kQkGroupsPerCu;
+}
 // turbo3: 64 two-value entries of 8 B, kLdsCopies8 copies (conflict-free);
 // turbo2: 256 four-value entries of 16 B, 8 copies (16 B lookups are served 16 lanes
 // per cycle, so lanes l and l + 8 may meet: the full 16 copies would take 64 KB and
@@ -995,7 +1000,7 @@ __device__ __forceinline__ f4_t qk_unit(const h8_t (&A)[8], const uint32_t *w, u
 // workgroup scores cache rows [blockIdx.y * tpg, +tpg) of one (sequence, kv head) for up
 // to eight query heads (pass blockIdx.x % passes).
 template <int BITS, int MF>
-__global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uint8_t *__restrict__ k_codes,
+__global__ __launch_bounds__(256, qk_groups_per_cu(BITS, MF)) void qk_kernel(const uint8_t *__restrict__ k_codes,
                                                     const uint16_t *__restrict__ k_norms,
                                                     const uint16_t *__restrict__ q,
                                                     float *__restrict__ scores, uint32_t Hkv,
@@ -1061,17 +1066,16 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
         if constexpr (!FAST)
             nr = ld_stream(k_norms + blk0 + __umul24(r, m));
     };
-    // Batched path: a batch of kQkDepth units holds 128 (row, block) pairs, whose norms
-    // come in two loads (elements e0 + lane and e0 + 64 + lane from the batch's first
-    // row, clamped to the last element of the wave's last row, as the codes); each unit
-    // takes its pair's norm from the lane that holds it.  A separate small load per unit
-    // would cost the memory pipeline about as much as the unit's codes.
-    static_assert(kQkDepth * 16 == 128, "two norm loads per batch");
-    auto fetch_norms = [&](uint32_t k, uint16_t &na, uint16_t &nb) {
+    // Batched path: a batch of kQkDepth units holds 64 (row, block) pairs, whose norms
+    // come in one load (element e0 + lane from the batch's first row, clamped to the
+    // last element of the wave's last row, as the codes); each unit takes its pair's
+    // norm from the lane that holds it.  A separate small load per unit would cost the
+    // memory pipeline about as much as the unit's codes.
+    static_assert(kQkDepth * 16 == 64, "one norm load per batch");
+    auto fetch_norms = [&](uint32_t k, uint16_t &na) {
         const size_t e0 = (row0 + first + 16u * (k / MD)) * MD;
         const size_t emax = (row0 + lastc) * MD + (MD - 1u);
         na = ld_stream(k_norms + min(e0 + lane, emax));
-        nb = ld_stream(k_norms + min(e0 + 64u + lane, emax));
     };
     uint16_t qpre[2][2] = {{0, 0}, {0, 0}};
     if constexpr (MF == 1)   // the queries first: their wait does not cover the codes
@@ -1080,12 +1084,12 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
     uint16_t nn[kQkDepth];
     // (16-bit, widened only where used: a widening right after the load would wait
     // for it there)
-    uint16_t nna = 0, nnb = 0;
+    uint16_t nna = 0;
 #pragma unroll
     for (int d = 0; d < kQkDepth; ++d)
         fetch(d, wn[d], nn[d]);
     if constexpr (FAST)
-        fetch_norms(0, nna, nnb);
+        fetch_norms(0, nna);
 
     __shared__ float lv[8];
     levels_to_lds(lv, cb);
@@ -1130,17 +1134,16 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
     float *const out_s = scores + ((size_t)b * Hq + h0 + sh) * T;
     // the source lane of the norm of (row group rg, block j) of a batch, and the score of
     // a finished row group into the stage
-    auto batch_norm = [&](int rg, int j, uint16_t na, uint16_t nb) -> float {
+    auto batch_norm = [&](int rg, int j, uint16_t na) -> float {
         const int src = (16 * rg + (int)n) * (int)MD + j;
-        const uint16_t nr16 = (uint16_t)__shfl((int)(uint32_t)(16 * rg * (int)MD < 64 ? na : nb),
-                                              src & 63, 64);
+        const uint16_t nr16 = (uint16_t)__shfl((int)(uint32_t)na, src, 64);
         return (float)__builtin_bit_cast(_Float16, nr16);
     };
 
     f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t k0 = 0;
     if constexpr (FAST) {
-        // Whole batches (128 / MF rows inside the wave's range, 16-byte aligned score
+        // Whole batches (64 / MF rows inside the wave's range, 16-byte aligned score
         // rows): the next batch's loads are unconditional (rows clamped inside the
         // chunk), every lane stores a 16-byte score line per pair of row groups (a lane
         // whose head is past the pass's last one writes that head's line again, with the
@@ -1152,7 +1155,7 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
         const uint32_t shf = min(sh, nh - 1u);
         float *const out_f = scores + ((size_t)b * Hq + h0 + shf) * T;
         uint32_t wc[kQkDepth][LW];
-        uint16_t nca = nna, ncb = nnb;
+        uint16_t nca = nna;
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d)
 #pragma unroll
@@ -1163,11 +1166,11 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
                 fetch(k0 + kQkDepth + d, wn[d], nn[d]);
-            fetch_norms(k0 + kQkDepth, nna, nnb);
+            fetch_norms(k0 + kQkDepth, nna);
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d) {
                 const int rg = d / (int)MD, jb = d % (int)MD;   // row group, block
-                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca, ncb);
+                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca);
                 acc = jb == 0 ? Du : acc + Du;
                 if (jb == (int)MD - 1) {
                     float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3];
@@ -1189,7 +1192,6 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
                 for (int i = 0; i < LW; ++i)
                     wc[d][i] = wn[d][i];
             nca = nna;
-            ncb = nnb;
         }
     }
     // Remaining units (all of them on the general path; at most one ragged batch on the
@@ -1204,13 +1206,13 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
                 wc[d][i] = wn[d][i];
             nc[d] = nn[d];
         }
-        const uint16_t nca = nna, ncb = nnb;
+        const uint16_t nca = nna;
         if (k0 + kQkDepth < nunits) {
 #pragma unroll
             for (int d = 0; d < kQkDepth; ++d)
                 fetch(k0 + kQkDepth + d, wn[d], nn[d]);
             if constexpr (FAST)
-                fetch_norms(k0 + kQkDepth, nna, nnb);
+                fetch_norms(k0 + kQkDepth, nna);
         }
 #pragma unroll
         for (int d = 0; d < kQkDepth; ++d) {
@@ -1218,7 +1220,7 @@ __global__ __launch_bounds__(256, qk_groups_per_cu(MF)) void qk_kernel(const uin
             if constexpr (FAST) {
                 const int rg = d / (int)MD, jb = d % (int)MD;
                 const uint32_t gi = k / MD;
-                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca, ncb);
+                const f4_t Du = qk_unit<BITS>(A[jb], wc[d], tcopy) * batch_norm(rg, jb, nca);
                 acc = jb == 0 ? Du : acc + Du;
                 if (jb == (int)MD - 1) {
                     // rows h (hi) and 8 + h (lo) sit in lanes l and l + 32: one swap pairs them
@@ -2018,7 +2020,7 @@ int launch_qk(int bits, const Signs &sg, const void *k_codes, const void *k_norm
     // batches of kQkDepth units per wave, at most 65535 row chunks.
     const int64_t step = (int64_t)kWavesPerGroup * 16 * (m >= kQkDepth ? 1 : kQkDepth / m);
     const int64_t pairs = B * Hkv * passes;
-    const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(m);
+    const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(bits, m);
     int64_t tpg = (T * pairs + round - 1) / round;
     tpg = tpg < (T + 65534) / 65535 ? (T + 65534) / 65535 : tpg;
     tpg = ((tpg + step - 1) / step) * step;

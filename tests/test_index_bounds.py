@@ -27,7 +27,7 @@ INTERNAL = os.path.join(ROOT, "kv_cache_quantization_block_amd", "csrc", "intern
 
 # constants of the kernels this replay assumes
 WAVES = 4                 # kWavesPerGroup
-QK_DEPTH = 8              # kQkDepth
+QK_DEPTH = 4              # kQkDepth
 QK_HEADS = 8              # kQkHeads
 QK_GROUPS_PER_CU = 4      # kQkGroupsPerCu
 # attn_groups_per_cu(bits, NHS, M), NHS = sets of four query heads (2 when G > 4)
@@ -53,12 +53,13 @@ def test_constants_match_the_kernels():
     assert "constexpr int attn_depth(int M) { return 4 / M; }" in src
     assert "constexpr int attn_rec(int M) { return 4 + kBlock * M; }" in src
     assert "if (tpg > 8192)" in src and "65535" in src
-    assert "constexpr int qk_groups_per_cu(int64_t m) { return m == 2 ? 3 : kQkGroupsPerCu; }" in src
+    assert "return m == 2 ? 3 : bits == 3 && m == 1 ? 5 : kQkGroupsPerCu;" in src
     # q.K's prefetch clamp, as replayed below
     assert "const uint32_t lastc = first < last ? last - 1u : t_end - 1u;" in src
     assert "const uint32_t tb = min(first + gi * 16u, lastc);" in src
     assert "const size_t emax = (row0 + lastc) * MD + (MD - 1u);" in src
-    assert "const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(m);" in src
+    assert "const int64_t round = (int64_t)cu_count() * qk_groups_per_cu(bits, m);" in src
+    assert "na = ld_stream(k_norms + min(e0 + lane, emax));" in src
 
 
 def cdiv(a, b):
@@ -94,12 +95,16 @@ N16, PART = LANE & 15, LANE >> 4
 
 # ---------------------------------------------------------------- q.K
 
-def qk_grid(B, Hkv, T, m, Hq, cu):
+def qk_groups_per_cu(bits, m):
+    return 3 if m == 2 else 5 if bits == 3 and m == 1 else QK_GROUPS_PER_CU
+
+
+def qk_grid(bits, B, Hkv, T, m, Hq, cu):
     G = Hq // Hkv
     passes = cdiv(G, QK_HEADS)
     step = WAVES * 16 * (1 if m >= QK_DEPTH else QK_DEPTH // m)
     pairs = B * Hkv * passes
-    rnd = cu * (3 if m == 2 else QK_GROUPS_PER_CU)
+    rnd = cu * qk_groups_per_cu(bits, m)
     tpg = cdiv(T * pairs, rnd)
     tpg = max(tpg, cdiv(T, 65535))
     tpg = max(rup(tpg, step), step)
@@ -132,7 +137,7 @@ def wave_contexts(nx, ny, passes, Hkv, G, T, Tc, rows):
 
 def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
     Hq, m, CB = Hkv * G, D // 128, 16 * bits
-    G_, passes, pairs, chunks, tpg = qk_grid(B, Hkv, T, m, Hq, cu)
+    G_, passes, pairs, chunks, tpg = qk_grid(bits, B, Hkv, T, m, Hq, cu)
     assert tpg % (WAVES * 16) == 0
     fast = m <= 2             # the batched path (one or two blocks per row)
     MD = m if fast else 1
@@ -172,12 +177,11 @@ def replay_qk(bits, B, Hkv, G, Tc, T, D, cu=256):
         codes.check(byte, width=4 * bits, align=4)
         if not fast:
             norms.check(blk0 + r * m)
-    if fast:   # a batch's norms: two loads per lane, clamped to the wave's last element
+    if fast:   # a batch's norms: one load per lane, clamped to the wave's last element
         emax = (row0 + lastc) * MD + (MD - 1)
         for k in range(0, kmax, QK_DEPTH):
             e0 = (row0 + first + 16 * (k // MD)) * MD
             norms.check(np.minimum(e0 + LANE, emax))
-            norms.check(np.minimum(e0 + 64 + LANE, emax))
             assert np.all(emax < B * Hkv * Tc * m)
     # score stores
     if fast:
@@ -382,7 +386,7 @@ def test_replay_catches_the_unclamped_head_store():
     pass reaches past the end of the buffer."""
     B, Hkv, G, T = 1, 1, 12, 40
     Hq = Hkv * G
-    G_, passes, pairs, chunks, tpg = qk_grid(B, Hkv, T, 1, Hq, 256)
+    G_, passes, pairs, chunks, tpg = qk_grid(3, B, Hkv, T, 1, Hq, 256)
     c = wave_contexts(pairs, chunks, passes, Hkv, G, T, T, tpg)
     sh = LANE >> 3
     head = c["h0"] + sh                      # the unclamped head of each score lane
