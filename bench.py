@@ -605,7 +605,8 @@ def one_layer(tq, gen, dev, stream, reps=20):
     ops.append(("append_turbo3", codec_bytes(2 * H * m, 3), lambda: tq.tq_encode(3, tok, c3, n3, T - 1)))
     ops.append(("qk_turbo3", qk_bytes(1, H, T, m, HQ, 3),
                 lambda: tq.tq_qk_scores(3, c3[0:1], n3[0:1], q, scale, scores)))
-    signs = np.where(np.random.default_rng(w.seed).random(128) < 0.5, -1.0, 1.0)
+    # the signs as the library's four words, converted once (as a serving loop would)
+    signs = tq.sign_words(np.where(np.random.default_rng(w.seed).random(128) < 0.5, -1.0, 1.0))
     b3 = bufs[3]
     rec = torch.empty(nblk * 50, dtype=torch.uint8, device=dev)
     extra_ops = [

@@ -161,7 +161,11 @@ def tq_codebook(type: int):
 
 def sign_words(signs):
     """128 diagonal entries of the randomised rotation H D (+1 / -1, or bools where True
-    means -1) -> the four 32-bit words the _rot calls take (bit p set <=> D_pp = -1)."""
+    means -1) -> the four 32-bit words the _rot calls take (bit p set <=> D_pp = -1).
+    Words made by an earlier call pass through unchanged, so a caller that launches
+    often can convert its signs once."""
+    if isinstance(signs, ctypes.Array) and signs._type_ is ctypes.c_uint32 and len(signs) == 4:
+        return signs
     if isinstance(signs, torch.Tensor):
         signs = signs.detach().cpu().numpy()
     v = np.asarray(signs)

@@ -357,7 +357,9 @@ __device__ __forceinline__ void store_enc_tile(const uint8_t *stage, uint32_t la
 // eight codes (24 / 16 bits, byte aligned), which go to the staged tile by byte writes.
 // The norm's sum of squares comes from the same loads (v_dot2 of exact fp16 squares)
 // and is summed over the four lane groups of a block in one fixed order.
-template <int BITS, bool ROT>
+// LOOP: the grid may give a wave several tiles (false: one tile per wave, so nothing
+// is prefetched for a next one).
+template <int BITS, bool ROT, bool LOOP>
 __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restrict__ x,
                                                             uint32_t nblocks, uint32_t row_blocks,
                                                             int64_t cache_row_blocks,
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
     for (;;) {
         const uint32_t b0 = tile * kEncTileBlocks;
         const uint32_t nb = min(nblocks - b0, (uint32_t)kEncTileBlocks);
-        const uint32_t next = tile + stride;
+        const uint32_t next = LOOP ? tile + stride : ntiles;
         float nrm[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -1909,9 +1911,13 @@ int cu_count()
 //     so the waves' load, compute and store phases drift apart.  A persistent grid
 //     of two groups per CU, each wave prefetching its next tile, runs the same
 //     eight-layer encode at 5.28 TB/s against 5.6 TB/s for this one (8 to 24 layers
-//     gain 3-7 %, one layer is unchanged).  The randomised-rotation variant keeps
-//     a persistent grid of two groups per CU: its sign masks take it to 138-142
-//     VGPRs, three waves per SIMD, where one tile per wave runs 13 % slower.
+//     gain 3-7 %, one layer is unchanged).  The randomised-rotation variant needs
+//     its sign masks too: with the tile loop (a capped grid) that takes it to 142
+//     VGPRs, three waves per SIMD, so a grid of one tile per wave launches its build
+//     without the loop (LOOP = false: no load registers kept for a next tile, 105
+//     VGPRs, four waves per SIMD), 11-16 % faster than the capped loop.  The plain
+//     encoder's loop-free build (72 VGPRs) measured no faster than the loop at
+//     126, so it always runs the loop.
 //   decode: no cap either, one 32-block tile per wave (80-106 VGPRs and 20 / 33 KB of
 //     LDS allow four to six groups per CU); caps of 5, 10 or 20 groups per CU
 //     measured slower on 8- to 48-layer caches.
@@ -1971,7 +1977,7 @@ int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int
     const Codebook *cb = codebook(bits);
     hipStream_t s = (hipStream_t)stream;
     static const int per_cu = groups_per_cu("TQ_ENCODE_GROUPS_PER_CU", 0);
-    static const int per_cu_rot = groups_per_cu("TQ_ENCODE_ROT_GROUPS_PER_CU", 2);
+    static const int per_cu_rot = groups_per_cu("TQ_ENCODE_ROT_GROUPS_PER_CU", 0);
     const bool rot = has_signs(sg);
     dim3 grid(grid_for(nblocks, kEncTileBlocks, rot ? per_cu_rot : per_cu)), block(256);
     auto launch = [&](auto kern) {
@@ -1979,10 +1985,18 @@ int launch_encode(int bits, const Signs &sg, const void *x, int64_t nblocks, int
                       (uint32_t)row_blocks, cache_row_blocks, t0_blocks, (uint8_t *)codes,
                       (uint16_t *)norms, *cb, sg);
     };
-    if (bits == 3)
-        rot ? launch(encode_kernel<3, true>) : launch(encode_kernel<3, false>);
-    else
-        rot ? launch(encode_kernel<2, true>) : launch(encode_kernel<2, false>);
+    const bool loop = (int64_t)grid.x * kWavesPerGroup * kEncTileBlocks < nblocks;
+    if (bits == 3) {
+        if (rot)
+            loop ? launch(encode_kernel<3, true, true>) : launch(encode_kernel<3, true, false>);
+        else
+            launch(encode_kernel<3, false, true>);
+    } else {
+        if (rot)
+            loop ? launch(encode_kernel<2, true, true>) : launch(encode_kernel<2, true, false>);
+        else
+            launch(encode_kernel<2, false, true>);
+    }
     return (int)hipGetLastError();
 }
 

@@ -262,6 +262,11 @@ def test_sign_words_bit_layout():
         tq.sign_words(np.ones(127))
     with pytest.raises(ValueError):
         tq.sign_words(np.full(128, 0.5))
+    # words from an earlier call pass through as they are (no conversion per launch)
+    words = tq.sign_words(d)
+    assert tq.sign_words(words) is words
+    with pytest.raises(ValueError):
+        tq.sign_words((ctypes.c_uint32 * 3)(1, 2, 3))
 
 
 def test_record_validation(L):

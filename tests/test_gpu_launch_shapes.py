@@ -2,14 +2,15 @@
 
 encode_kernel and decode_kernel take their 32-block tiles either one per wave (the
 one-shot grid) or several per wave (a grid capped at some workgroups per compute
-unit; the encoder then stores one tile while it loads the next).  The
-randomised-rotation encode uses the capped grid (two workgroups per CU) by default,
-the plain encode and decode only when TQ_ENCODE_GROUPS_PER_CU /
-TQ_DECODE_GROUPS_PER_CU ask for it or past 2^22 workgroups.  So:
-- in this process, the rotation encode runs several tiles per wave at a size the
-  oracle checks in full;
+unit; the encoder then stores one tile while it loads the next).  All of them use
+the one-shot grid by default (the randomised-rotation encode in its build without
+the tile loop), and the capped grid only when TQ_ENCODE_GROUPS_PER_CU,
+TQ_ENCODE_ROT_GROUPS_PER_CU or TQ_DECODE_GROUPS_PER_CU ask for it, or past 2^22
+workgroups.  So:
+- in this process, the rotation encode (one tile per wave) is checked against the
+  oracle in full;
 - a child process whose environment caps the plain grids at one workgroup per CU
-  (four tiles per wave) and lifts the cap of the rotation encode (one tile per wave)
+  (four tiles per wave) and the rotation encode at two (most waves take two tiles)
   repeats the plain and rotation calls; every output buffer must match this
   process's bit for bit (each block's arithmetic is the same whichever wave does it).
 """
@@ -41,9 +42,8 @@ def _gpu():
 
 @pytest.mark.parametrize("bits", [3, 2])
 @pytest.mark.parametrize("layout", ["contiguous", "offset"])
-def test_rot_encode_several_tiles_per_wave(bits, layout):
-    """4,098 tiles against 2,048 waves (two groups per CU): most waves take two
-    tiles, and the last tile is ragged."""
+def test_rot_encode_one_tile_per_wave(bits, layout):
+    """4,098 tiles, one per wave, the last one ragged."""
     L, H, T, D = child.L, child.H, child.T, child.D
     Tc, t0 = child.LAYOUTS[layout]
     d = child.signs()
@@ -61,7 +61,7 @@ def test_rot_encode_several_tiles_per_wave(bits, layout):
     on = np.full(gn.shape, child.SENT_NORM, np.float16)
     dist = oracle.encode(bits, xn, oc, on, t0=t0, want_dist=True, signs=d)
     rows = slice(t0, t0 + T)
-    what = f"rot encode, several tiles per wave, {layout}"
+    what = f"rot encode, one tile per wave, {layout}"
     st = check_codes(bits, gc[:, :, rows], oc[:, :, rows], dist.reshape(L, H, T, D // 128, 128), what)
     st.update(check_norms(gn[:, :, rows], on[:, :, rows], xn, what))
     assert np.all(gc[:, :, :t0] == child.SENT_CODE) and np.all(gc[:, :, t0 + T:] == child.SENT_CODE)
@@ -74,8 +74,8 @@ def test_rot_encode_several_tiles_per_wave(bits, layout):
 def test_other_grid_shapes_give_the_same_bytes():
     here = child.run_all()
     env = dict(os.environ, TQ_ENCODE_GROUPS_PER_CU="1", TQ_DECODE_GROUPS_PER_CU="1",
-               TQ_ENCODE_ROT_GROUPS_PER_CU="0")
-    print("child: plain grids at one group per CU, rotation encode one-shot", flush=True)
+               TQ_ENCODE_ROT_GROUPS_PER_CU="2")
+    print("child: plain grids at one group per CU, rotation encode at two", flush=True)
     r = subprocess.run([sys.executable, os.path.join(HERE, "_launch_shape_child.py")], env=env,
                        capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-3000:]
