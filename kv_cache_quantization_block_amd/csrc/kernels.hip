@@ -376,6 +376,14 @@ __global__ __launch_bounds__(256, 3) void encode_kernel(const uint8_t *__restric
     const uint32_t ntiles = (nblocks + kEncTileBlocks - 1) / kEncTileBlocks;
     const uint32_t stride = gridDim.x * kWavesPerGroup;
     uint32_t tile = blockIdx.x * kWavesPerGroup + wave;
+    // turbo2 with one tile per wave: in each whole run of 32 tiles (8 workgroups, which
+    // the dispatcher deals to the 8 XCDs in turn) tile 8 w + x goes to wave w of the
+    // run's x-th workgroup, so consecutive 8 KB tiles sit on different XCDs.  turbo2
+    // measured 1.5-3 % faster so, turbo3 0.4-1.3 % slower, and keeps the plain order.
+    if constexpr (BITS == 2) {
+        if (gridDim.x * kWavesPerGroup >= ntiles && (tile | 31u) < ntiles)
+            tile = (tile & ~31u) + wave * 8u + (blockIdx.x & 7u);
+    }
     if (tile >= ntiles)
         return;
     uint8_t *stage = stage_all[wave];
