@@ -12,7 +12,8 @@ tiles and workspace records, the combine's reads and writes -- and checks, for
 every lane of every workgroup, that each access stays inside its buffer, for every
 shape the GPU tests, the smoke check, the quality harness and the benchmark launch.
 The constants it assumes are read back from kernels.hip, so a change there that the
-replay does not follow fails here.
+replay does not follow fails here.  It also replays which tiles the encoder's waves
+take (turbo2 reorders them), and checks that every tile is encoded exactly once.
 """
 import math
 import os
@@ -392,3 +393,41 @@ def test_replay_catches_the_unclamped_head_store():
     head = c["h0"] + sh                      # the unclamped head of each score lane
     assert (head >= Hq).any()                # the second pass's lanes past head 11
     assert ((head * T).max() + T) > B * Hq * T
+
+
+# ---------------------------------------------------------------- encoder tile order
+
+def encoder_tiles(bits, nblocks, grid, tile_blocks=32):
+    """The tiles each wave of encode_kernel takes, restated: wave w of workgroup x starts
+    at tile 4 x + w, which turbo2 remaps inside each whole run of 32 tiles when the grid
+    gives every wave one tile, then steps by the grid's wave count."""
+    ntiles = cdiv(nblocks, tile_blocks)
+    stride = grid * WAVES
+    taken = []
+    for x in range(grid):
+        for w in range(WAVES):
+            t = x * WAVES + w
+            if bits == 2 and stride >= ntiles and (t | 31) < ntiles:
+                t = (t & ~31) + w * 8 + (x & 7)
+            while t < ntiles:
+                taken.append(t)
+                t += stride
+    return ntiles, taken
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("nblocks", [1, 31, 32, 33, 1000, 1024, 1056, 131136, 25165824 // 64])
+def test_encoder_takes_every_tile_once(bits, nblocks):
+    """One tile per wave (the default grid) and a grid capped at one or two workgroups per
+    CU: every tile of the input is encoded exactly once, whatever the order."""
+    ntiles = cdiv(nblocks, 32)
+    for grid in (cdiv(ntiles, WAVES), min(cdiv(ntiles, WAVES), 256), min(cdiv(ntiles, WAVES), 512)):
+        n, taken = encoder_tiles(bits, nblocks, grid)
+        assert sorted(taken) == list(range(n)), (bits, nblocks, grid)
+
+
+def test_encoder_tile_order_matches_the_kernel():
+    src = open(KERNELS).read()
+    assert "if (gridDim.x * kWavesPerGroup >= ntiles && (tile | 31u) < ntiles)" in src
+    assert "tile = (tile & ~31u) + wave * 8u + (blockIdx.x & 7u);" in src
+    assert "uint32_t tile = blockIdx.x * kWavesPerGroup + wave;" in src
